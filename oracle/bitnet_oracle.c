@@ -1,0 +1,316 @@
+/*
+ * bitnet_oracle.c -- plain CPU statement of the H-BitLinear forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or calls this
+ * file, and this file includes nothing of the product.  Only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load it (as liboracle_bitnet.so through ctypes).
+ *
+ * Every function follows one passage of the source pages, cited by page and section:
+ *   [v2-news]   BitNet v2 news write-up (Xinzhiyuan, kaiyunao.com mirror): the H-BitLinear
+ *               passage (online Hadamard before activation quantisation; +1/-1 entries with
+ *               mutually orthogonal rows; INT4 activations for every linear but embeddings).
+ *   [v2-abs]    "BitNet v2: Native 4-bit Activations with Hadamard Transformation for 1-bit
+ *               LLMs" (chatpaper.ai abstract): H-BitLinear applies an online Hadamard
+ *               transformation prior to activation quantization.
+ *   [2B4T-1.1]  BitNet b1.58 2B4T write-up (itdecent.cn), section 1.1 "ternary weights and
+ *               1.58-bit storage": five ternary weights packed into one byte, worked example
+ *               (2,0,1,2,1) -> 178 = 0b10110010.
+ *   [2B4T-1.2]  same page, section 1.2 "BitLinear": weights by absmean to 1.58 bit,
+ *               activations by absmax to 8 bit (W1.58A8); x1 is an add, x-1 a subtract,
+ *               x0 is skipped.
+ *   [b158]      BitNet b1.58 summary of arXiv 2402.17764 (gptget.net), "method" and
+ *               "method details": absmean quantisation constrains weights to {-1,0,+1};
+ *               BitLinear replaces nn.Linear.
+ *
+ * Where the pages are silent the plainest reading is taken; each such reading is noted at
+ * the function that makes it.  Floating point follows the precision the layer computes in
+ * (fp32 activations and scales; the weight mean is accumulated in double).  Build with
+ * -O2 -ffp-contract=off and no fast-math so that every fp32 operation is one IEEE rounding.
+ *
+ * Loops over independent rows carry an OpenMP pragma; that changes no result.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------- */
+/* Base-3 byte code [2B4T-1.1].                                                           */
+/* A byte holds five ternary digits d_0..d_4 (d = t + 1 in {0,1,2}), d_0 most significant: */
+/* byte = 81 d_0 + 27 d_1 + 9 d_2 + 3 d_3 + d_4.  The worked example (2,0,1,2,1) -> 178    */
+/* fixes the digit order (least-significant-first would give 146).                          */
+/* ------------------------------------------------------------------------------------- */
+
+int bitnet_ref_encode5(const int *digits)
+{
+    int v = 0;
+    for (int i = 0; i < 5; i++) {
+        if (digits[i] < 0 || digits[i] > 2) return -1;
+        v = v * 3 + digits[i];
+    }
+    return v;
+}
+
+/* Returns 0 on success, -1 for a byte that is not a base-3 code (> 242). */
+int bitnet_ref_decode5(int byte, int *digits)
+{
+    if (byte < 0 || byte > 242) return -1;
+    int v = byte;
+    for (int i = 4; i >= 0; i--) {
+        digits[i] = v % 3;
+        v /= 3;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* absmean ternarisation [b158 method; 2B4T-1.2].                                          */
+/* gamma = mean |W| over the whole matrix (one scale per tensor: the pages give no finer     */
+/* granularity), summed in double in row-major order; t = RoundClip(W / gamma, -1, 1) with    */
+/* an fp32 division and round-half-to-even.  The pages give no epsilon: a zero matrix (gamma */
+/* == 0) ternarises to all zeros.                                                           */
+/* ------------------------------------------------------------------------------------- */
+
+float bitnet_ref_absmean(const float *W, int64_t count)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < count; i++) s += fabs((double)W[i]);
+    return (float)(s / (double)count);
+}
+
+void bitnet_ref_ternarize(const float *W, int N, int K, int8_t *t, float *gamma_out)
+{
+    int64_t count = (int64_t)N * K;
+    float g = bitnet_ref_absmean(W, count);
+    *gamma_out = g;
+    for (int64_t i = 0; i < count; i++) {
+        if (g == 0.0f) { t[i] = 0; continue; }
+        float r = nearbyintf(W[i] / g);
+        t[i] = (int8_t)(r > 1.0f ? 1 : (r < -1.0f ? -1 : (int)r));
+    }
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Packed weight layout.  The pages fix the byte code (five trits, base 3, MSB first) but    */
+/* not which five weights of a row share a byte.  Reading taken: a row is cut into blocks of  */
+/* 320 weights (64 bytes); byte b of block B holds the weights at k = 320 B + b + 64 i as     */
+/* digit i (i = 0..4).  Weights past the end of the row (k >= K) are t = 0 (digit 1).         */
+/* Row n occupies bytes [n * 64 * ceil(K/320), (n+1) * 64 * ceil(K/320)).                    */
+/* ------------------------------------------------------------------------------------- */
+
+int64_t bitnet_ref_row_bytes(int K) { return 64 * (int64_t)((K + 319) / 320); }
+
+int64_t bitnet_ref_packed_bytes(int N, int K) { return (int64_t)N * bitnet_ref_row_bytes(K); }
+
+void bitnet_ref_pack(const int8_t *t, int N, int K, uint8_t *packed)
+{
+    int64_t rb = bitnet_ref_row_bytes(K);
+    for (int n = 0; n < N; n++) {
+        for (int64_t j = 0; j < rb; j++) {
+            int64_t block = j / 64, b = j % 64;
+            int digits[5];
+            for (int i = 0; i < 5; i++) {
+                int64_t k = 320 * block + b + 64 * i;
+                int tv = (k < K) ? t[(int64_t)n * K + k] : 0;
+                digits[i] = tv + 1;
+            }
+            packed[(int64_t)n * rb + j] = (uint8_t)bitnet_ref_encode5(digits);
+        }
+    }
+}
+
+/* Inverse of bitnet_ref_pack.  Returns 0, or -1 if a byte is not a base-3 code or a padding */
+/* position holds a non-zero weight.                                                        */
+int bitnet_ref_unpack(const uint8_t *packed, int N, int K, int8_t *t)
+{
+    int64_t rb = bitnet_ref_row_bytes(K);
+    for (int n = 0; n < N; n++) {
+        for (int64_t j = 0; j < rb; j++) {
+            int64_t block = j / 64, b = j % 64;
+            int digits[5];
+            if (bitnet_ref_decode5(packed[(int64_t)n * rb + j], digits) != 0) return -1;
+            for (int i = 0; i < 5; i++) {
+                int64_t k = 320 * block + b + 64 * i;
+                if (k < K) t[(int64_t)n * K + k] = (int8_t)(digits[i] - 1);
+                else if (digits[i] != 1) return -1;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Online Hadamard transform [v2-news H-BitLinear passage; v2-abs].                         */
+/* H_n has +1/-1 entries and orthogonal rows; reading taken: the Sylvester matrix            */
+/* H[i][j] = (-1)^popcount(i & j), normalised by 1/sqrt(n), applied to each token row.       */
+/* The fast transform runs its radix-2 stages with the butterfly span h = 1, 2, 4, ..., n/2  */
+/* (low index bit first); the pages give no order, and this one is what the in-place         */
+/* butterfly computes.  Unnormalised here; bitnet_ref_hadamard applies the 1/sqrt(n) once,   */
+/* after the last stage, as the fp32 constant (float)(1/sqrt((double)n)).                    */
+/* ------------------------------------------------------------------------------------- */
+
+void bitnet_ref_fwht(float *x, int n)
+{
+    for (int h = 1; h < n; h *= 2) {
+        for (int base = 0; base < n; base += 2 * h) {
+            for (int j = base; j < base + h; j++) {
+                float a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+        }
+    }
+}
+
+void bitnet_ref_fwht_f64(double *x, int n)
+{
+    for (int h = 1; h < n; h *= 2) {
+        for (int base = 0; base < n; base += 2 * h) {
+            for (int j = base; j < base + h; j++) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+        }
+    }
+}
+
+float bitnet_ref_hadamard_scale(int n) { return (float)(1.0 / sqrt((double)n)); }
+
+void bitnet_ref_hadamard(float *x, int n)
+{
+    bitnet_ref_fwht(x, n);
+    float c = bitnet_ref_hadamard_scale(n);
+    for (int k = 0; k < n; k++) x[k] = x[k] * c;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Per-token absmax quantisation [2B4T-1.2 (8 bit, absmax); v2-news (4 bit for all          */
+/* linears)].  The 4-bit formula is missing from the page; reading taken: the same absmax    */
+/* rule with Qp = 2^(b-1) - 1 (127 or 7) and codes clipped to [-Qp-1, Qp].                   */
+/*   gamma = max_k |x_k|;  inv = Qp / gamma (fp32 division);                                */
+/*   q_k = clamp(rne(x_k * inv), -Qp-1, Qp);  scale = gamma / Qp (fp32 division).           */
+/* No epsilon: an all-zero row has gamma = 0, codes 0 and scale 0.                          */
+/* ------------------------------------------------------------------------------------- */
+
+void bitnet_ref_quantize_row(const float *x, int K, int bits, int8_t *q, float *scale_out)
+{
+    int qp = (1 << (bits - 1)) - 1;
+    float g = 0.0f;
+    for (int k = 0; k < K; k++) {
+        float a = fabsf(x[k]);
+        if (a > g) g = a;
+    }
+    if (g == 0.0f) {
+        for (int k = 0; k < K; k++) q[k] = 0;
+        *scale_out = 0.0f;
+        return;
+    }
+    float inv = (float)qp / g;
+    for (int k = 0; k < K; k++) {
+        float r = nearbyintf(x[k] * inv);
+        int v = (int)r;
+        if (v > qp) v = qp;
+        if (v < -qp - 1) v = -qp - 1;
+        q[k] = (int8_t)v;
+    }
+    *scale_out = g / (float)qp;
+}
+
+/* INT4 codes two to a byte: low nibble holds the even k, high nibble the odd k (two's       */
+/* complement nibbles).  The pages say only that activations are 4-bit.                     */
+void bitnet_ref_pack_int4(const int8_t *q, int64_t count, uint8_t *out)
+{
+    for (int64_t i = 0; i < count / 2; i++)
+        out[i] = (uint8_t)((q[2 * i] & 0xF) | ((q[2 * i + 1] & 0xF) << 4));
+}
+
+void bitnet_ref_unpack_int4(const uint8_t *in, int64_t count, int8_t *q)
+{
+    for (int64_t i = 0; i < count / 2; i++) {
+        int lo = in[i] & 0xF, hi = in[i] >> 4;
+        q[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+        q[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+    }
+}
+
+/* Activation stage of H-BitLinear for M token rows: optional normalised Hadamard, then      */
+/* absmax quantisation.  q is M x K int8 (one code per byte, unpacked); xh (M x K fp32, may   */
+/* be NULL) receives the post-Hadamard values (the input itself when use_hadamard == 0).    */
+void bitnet_ref_quantize(const float *x, int M, int K, int bits, int use_hadamard,
+                         int8_t *q, float *scales, float *xh)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; m++) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)K);
+        memcpy(row, x + (int64_t)m * K, sizeof(float) * (size_t)K);
+        if (use_hadamard) bitnet_ref_hadamard(row, K);
+        if (xh) memcpy(xh + (int64_t)m * K, row, sizeof(float) * (size_t)K);
+        bitnet_ref_quantize_row(row, K, bits, q + (int64_t)m * K, &scales[m]);
+        free(row);
+    }
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Ternary matrix product [2B4T-1.2]: with weights in {-1,0,+1} a product term is an add     */
+/* (t = +1), a subtract (t = -1) or nothing (t = 0).  acc[m][n] = sum_k q[m][k] t[n][k] in   */
+/* int32; t is N x K (nn.Linear convention, [b158 method details]).                          */
+/* ------------------------------------------------------------------------------------- */
+
+void bitnet_ref_gemm(const int8_t *q, const int8_t *t, int M, int N, int K, int32_t *acc)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; m++) {
+        const int8_t *qr = q + (int64_t)m * K;
+        for (int n = 0; n < N; n++) {
+            const int8_t *tr = t + (int64_t)n * K;
+            int32_t s = 0;
+            for (int k = 0; k < K; k++) {
+                if (tr[k] == 1) s += qr[k];
+                else if (tr[k] == -1) s -= qr[k];
+            }
+            acc[(int64_t)m * N + n] = s;
+        }
+    }
+}
+
+/* Dequantisation: y = (float(acc) * scale_x[m]) * gamma_w, left to right in fp32.  The      */
+/* block has no bias term [v2-news: LLaMA-like components with the bias removed].            */
+void bitnet_ref_epilogue(const int32_t *acc, const float *scales, float gamma_w, int M, int N,
+                         float *y)
+{
+    for (int m = 0; m < M; m++)
+        for (int n = 0; n < N; n++) {
+            int64_t i = (int64_t)m * N + n;
+            y[i] = ((float)acc[i] * scales[m]) * gamma_w;
+        }
+}
+
+/* The whole forward for a packed weight matrix: unpack, activation stage, ternary product,  */
+/* dequantisation.  Returns 0, or -1 if the packed buffer does not decode.                  */
+int bitnet_ref_forward(const float *x, int M, int K, int N, int bits, int use_hadamard,
+                       const uint8_t *packed, float gamma_w, float *y)
+{
+    int8_t *t = (int8_t *)malloc((size_t)N * (size_t)K);
+    int8_t *q = (int8_t *)malloc((size_t)M * (size_t)K);
+    float *s = (float *)malloc(sizeof(float) * (size_t)M);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)M * (size_t)N);
+    int rc = bitnet_ref_unpack(packed, N, K, t);
+    if (rc == 0) {
+        bitnet_ref_quantize(x, M, K, bits, use_hadamard, q, s, NULL);
+        bitnet_ref_gemm(q, t, M, N, K, acc);
+        bitnet_ref_epilogue(acc, s, gamma_w, M, N, y);
+    }
+    free(t); free(q); free(s); free(acc);
+    return rc;
+}
+
+/* Number of OpenMP threads a parallel region here uses (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int bitnet_ref_num_threads(void) { return omp_get_max_threads(); }
+void bitnet_ref_set_num_threads(int n) { omp_set_num_threads(n); }
+#else
+int bitnet_ref_num_threads(void) { return 1; }
+void bitnet_ref_set_num_threads(int n) { (void)n; }
+#endif

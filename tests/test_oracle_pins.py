@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle to facts the source pages and mathematics fix.
+
+None of these tests re-types the oracle's formulas: each checks the oracle against a printed
+example, a closed form, an invariant, a brute-force count or an independent library routine.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------- base-3 byte code ----
+
+def test_worked_example_178():
+    g = read_golden("base3_worked_example.txt")
+    digits = [int(v) for v in g["digits"]]
+    byte = int(g["byte"][0])
+    assert oracle.encode5(digits) == byte
+    assert format(byte, "08b") == g["binary"][0]
+    assert list(oracle.decode5(byte)) == digits
+    # least-significant-first order would give a different byte: the example fixes the order
+    assert oracle.encode5(digits[::-1]) != byte
+
+
+def test_storage_efficiency_closed_form():
+    g = read_golden("base3_worked_example.txt")
+    eff = 5 * math.log2(3) / 8
+    assert round(100 * eff, 2) == float(g["efficiency_percent"][0])
+    assert 3 ** 5 <= 256                       # five trits fit in a byte
+    assert 3 ** 6 > 256                        # six do not
+    # 64 bytes per 320 weights: 1.6 bits per weight, 10x less than fp16
+    for K in (320, 640, 3200):
+        assert oracle.row_bytes(K) * 8 / K == pytest.approx(1.6)
+        assert 16 / (oracle.row_bytes(K) * 8 / K) == pytest.approx(10.0)
+
+
+def test_byte_code_is_bijection_onto_0_242():
+    seen = {}
+    for a in range(3):
+        for b in range(3):
+            for c in range(3):
+                for d in range(3):
+                    for e in range(3):
+                        v = oracle.encode5([a, b, c, d, e])
+                        assert 0 <= v <= 242
+                        assert v not in seen
+                        seen[v] = (a, b, c, d, e)
+                        assert tuple(oracle.decode5(v)) == (a, b, c, d, e)
+    assert len(seen) == 243
+    for v in range(243, 256):
+        assert oracle.decode5(v) is None
+    assert oracle.encode5([3, 0, 0, 0, 0]) == -1
+
+
+def test_pack_groups_five_weights_per_byte():
+    # weights at k = 0, 64, 128, 192, 256 of row 0 share byte 0 (layout reading); with
+    # trits (1, -1, 0, 1, 0) = digits (2, 0, 1, 2, 1) that byte is the page's 178.
+    K = 320
+    t = np.zeros((2, K), np.int8)
+    t[0, [0, 64, 128, 192, 256]] = [1, -1, 0, 1, 0]
+    p = oracle.pack(t)
+    assert p.shape == (128,)
+    assert p[0] == 178
+    assert np.all(p[1:] == 121)                 # all-zero trits: digits 1,1,1,1,1 = 121
+    assert oracle.encode5([1, 1, 1, 1, 1]) == 121
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 5), (2, 64), (4, 319), (5, 320), (3, 321),
+                                 (7, 1000), (16, 4096)])
+def test_pack_roundtrip_and_size(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    p = oracle.pack(t)
+    assert p.size == N * 64 * ((K + 319) // 320)
+    assert p.max() <= 242
+    assert np.array_equal(oracle.unpack(p, N, K), t)
+
+
+def test_unpack_rejects_bad_bytes():
+    t = np.zeros((1, 10), np.int8)
+    p = oracle.pack(t)
+    p2 = p.copy(); p2[3] = 243
+    with pytest.raises(ValueError):
+        oracle.unpack(p2, 1, 10)
+    p3 = p.copy(); p3[20] = 0                    # a padding position holding t = -1
+    with pytest.raises(ValueError):
+        oracle.unpack(p3, 1, 10)
+
+
+# ------------------------------------------------------------- absmean ternarisation ----
+
+def test_ternary_values_and_exact_mean():
+    W = si.gaussian_weights(1, 64, 333)
+    t, g = oracle.ternarize(W)
+    assert set(np.unique(t)).issubset({-1, 0, 1})
+    exact = math.fsum(abs(float(v)) for v in W.ravel()) / W.size
+    assert g == np.float32(exact)
+
+
+def test_ternarize_scale_invariance():
+    W = si.gaussian_weights(2, 32, 128)
+    t, g = oracle.ternarize(W)
+    for e in (-3, 1, 7):
+        t2, g2 = oracle.ternarize(W * np.float32(2.0 ** e))
+        assert np.array_equal(t, t2)
+        assert g2 == np.float32(g * 2.0 ** e)
+
+
+def test_ternarize_zero_matrix():
+    t, g = oracle.ternarize(np.zeros((3, 7), np.float32))
+    assert g == 0 and not t.any()
+
+
+def test_ternarize_brute_force_thresholds():
+    # t = +1 above gamma/2, -1 below -gamma/2, 0 inside; checked in exact arithmetic away from
+    # the two boundaries (rounding of the fp32 quotient can only matter within an ulp of them)
+    W = si.gaussian_weights(3, 40, 50)
+    t, g = oracle.ternarize(W)
+    r = W.astype(np.float64) / float(g)
+    far = np.abs(np.abs(r) - 0.5) > 1e-6
+    expect = np.where(r > 0.5, 1, np.where(r < -0.5, -1, 0))
+    assert np.array_equal(t[far], expect[far])
+    # large ratios clip to +-1
+    W2 = W.copy(); W2[0, 0] = 100 * g; W2[0, 1] = -100 * g
+    t2, _ = oracle.ternarize(W2)
+    assert t2[0, 0] == 1 and t2[0, 1] == -1
+
+
+def test_gaussian_zero_fraction_closed_form():
+    # For W ~ N(0, s^2): gamma = s sqrt(2/pi); P(t = 0) = P(|Z| < sqrt(2/pi)/2) = 2 Phi(.) - 1
+    W = si.gaussian_weights(2, 4096, 4096)
+    t, _ = oracle.ternarize(W)
+    frac = float(np.mean(t == 0))
+    c = 0.5 * math.sqrt(2.0 / math.pi)
+    expect = math.erf(c / math.sqrt(2.0))
+    assert abs(expect - 0.3101) < 1e-4
+    assert abs(frac - expect) < 2e-3
+    # and the signs are balanced
+    assert abs(float(np.mean(t == 1)) - float(np.mean(t == -1))) < 2e-3
+
+
+# -------------------------------------------------------------- Hadamard transform ----
+
+def _sylvester(n):
+    H = np.array([[1]], dtype=np.int64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_hadamard_entries_and_orthogonality_dense():
+    g = read_golden("hadamard_definition.txt")
+    for n in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        rows = oracle.fwht(np.eye(n, dtype=np.float32)).astype(np.int64)
+        assert set(np.unique(rows)).issubset({int(v) for v in g["entries"]})
+        gram = rows @ rows.T
+        assert np.array_equal(gram, n * np.eye(n, dtype=np.int64))
+        # Sylvester closed form H[i][j] = (-1)^popcount(i & j)
+        i = np.arange(n)[:, None]; j = np.arange(n)[None, :]
+        pc = np.vectorize(lambda v: bin(v).count("1"))(i & j)
+        assert np.array_equal(rows, np.where(pc % 2 == 0, 1, -1))
+
+
+def test_fwht_equals_dense_matmul_small():
+    rng = np.random.default_rng(5)
+    for n in (2, 4, 8, 16, 32, 64):
+        x = rng.integers(-50, 51, size=(9, n)).astype(np.float32)
+        dense = x.astype(np.int64) @ _sylvester(n)
+        assert np.array_equal(oracle.fwht(x), dense.astype(np.float32))
+        # normalised: one fp32 multiply by the rounded 1/sqrt(n)
+        c = np.float32(1.0 / math.sqrt(n))
+        assert oracle.hadamard_scale(n) == c
+        assert np.array_equal(oracle.hadamard(x), dense.astype(np.float32) * c)
+
+
+@pytest.mark.parametrize("n", [2 ** p for p in range(1, 15)])
+def test_h_ht_equals_n_identity(n):
+    # H H^T = n I, checked column by column as FWHT(FWHT(e_j)) = n e_j (exact integers)
+    for j in sorted({0, 1, n // 3, n // 2, n - 1}):
+        e = np.zeros(n, np.float32); e[j] = 1
+        r = oracle.fwht(oracle.fwht(e))
+        expect = np.zeros(n, np.float32); expect[j] = n
+        assert np.array_equal(r, expect)
+
+
+def test_normalised_transform_is_involution():
+    rng = np.random.default_rng(7)
+    for n in (4, 16, 64, 256, 1024, 4096, 16384):     # n = 4^k: 1/sqrt(n) is a power of two
+        x = rng.integers(-100, 101, size=(2, n)).astype(np.float32)
+        assert np.array_equal(oracle.hadamard(oracle.hadamard(x)), x)
+    for n in (2, 8, 32, 512, 8192):                    # otherwise within a few ulp
+        x = rng.standard_normal((2, n)).astype(np.float32)
+        back = oracle.hadamard(oracle.hadamard(x))
+        assert np.max(np.abs(back - x)) <= 8 * np.finfo(np.float32).eps * np.max(np.abs(x)) * math.log2(n)
+
+
+def test_parseval_and_fp64_error_bound():
+    rng = np.random.default_rng(9)
+    for n in (256, 4096, 16384):
+        x = rng.standard_normal((3, n)).astype(np.float32)
+        y = oracle.hadamard(x)
+        assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+        exact = oracle.fwht_f64(x.astype(np.float64)) / math.sqrt(n)
+        # each output is a sum of n terms formed by log2(n) rounded additions
+        bound = (math.log2(n) + 2) * np.finfo(np.float32).eps * np.sum(np.abs(x), axis=1, keepdims=True) / math.sqrt(n)
+        assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_spike_is_spread_flat():
+    # a single outlier channel c e_j maps to a vector whose entries all have magnitude c/sqrt(n)
+    for n in (256, 4096, 16384):
+        for j in (0, 3, n - 1):
+            x = np.zeros(n, np.float32); x[j] = 40.0
+            y = oracle.hadamard(x)
+            assert np.all(np.abs(y) == np.float32(40.0 / math.sqrt(n)))
+
+
+# --------------------------------------------------------------- absmax quantisation ----
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_closed_forms(bits):
+    qp = 2 ** (bits - 1) - 1
+    x = si.wo_activations(8, 4096)
+    for row in x:
+        q, s = oracle.quantize_row(row, bits)
+        g = np.max(np.abs(row))
+        assert s == np.float32(g / np.float32(qp))
+        imax = int(np.argmax(np.abs(row)))
+        assert q[imax] == (qp if row[imax] > 0 else -qp)
+        assert q.min() >= -qp - 1 and q.max() <= qp
+        err = np.abs(row.astype(np.float64) - float(s) * q.astype(np.float64))
+        assert np.all(err <= 0.5 * float(s) * (1 + 1e-5))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_integer_grid_is_lossless(bits):
+    qp = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(bits)
+    x = rng.integers(-qp, qp + 1, size=(6, 512)).astype(np.float32)
+    x[:, 17] = qp                                        # row max is exactly Qp
+    q, s = oracle.quantize(x, bits, False)
+    assert np.all(s == 1.0)
+    assert np.array_equal(q.astype(np.float32), x)
+
+
+def test_quantize_zero_row_and_sign_symmetry():
+    x = np.zeros((2, 64), np.float32)
+    x[1] = np.linspace(-3, 3, 64)
+    q, s = oracle.quantize(x, 8, False)
+    assert s[0] == 0 and not q[0].any()
+    qn, sn = oracle.quantize(-x, 8, False)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+
+
+def test_int4_nibble_layout():
+    q = np.array([[1, -1, 7, -8, 0, 3]], np.int8)
+    b = oracle.pack_int4(q)
+    assert list(b[0]) == [0xF1, 0x87, 0x30]
+    assert np.array_equal(oracle.unpack_int4(b, 6), q)
+
+
+# ------------------------------------------------------------------- ternary product ----
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (16, 33, 320), (5, 8, 1000)])
+def test_add_sub_skip_equals_integer_matmul(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    acc = oracle.gemm(q, t)
+    assert np.array_equal(acc, q.astype(np.int64) @ t.astype(np.int64).T)
+
+
+def test_gemm_extremes():
+    K = 16384
+    q = np.full((1, K), -128, np.int8)
+    t = np.full((2, K), 1, np.int8); t[1] = -1
+    acc = oracle.gemm(q, t)
+    assert acc[0, 0] == -128 * K and acc[0, 1] == 128 * K
+
+
+# ----------------------------------------------------------------------- end to end ----
+
+def test_forward_integer_grid_without_hadamard():
+    # x on the integer grid with row max Qp: s = 1 exactly, so y = gamma_w * (x t^T) exactly
+    rng = np.random.default_rng(11)
+    M, K, N = 4, 640, 24
+    x = rng.integers(-127, 128, size=(M, K)).astype(np.float32); x[:, 0] = 127
+    W = si.gaussian_weights(1, N, K)
+    packed, gw, t = oracle.pack_weights(W)
+    y = oracle.forward(x, packed, gw, N, 8, False)
+    exact = (x.astype(np.int64) @ t.astype(np.int64).T).astype(np.float32) * gw
+    assert np.array_equal(y, exact)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_hadamard_row_closed_form(bits):
+    # x = a * H[j, :]: the normalised transform gives a sqrt(K) e_j, the code is +-Qp at j,
+    # the scale a sqrt(K) / Qp, so y[n] = a sqrt(K) t[n, j] gamma_w
+    K, N = 1024, 40
+    H = oracle.fwht(np.eye(K, dtype=np.float32))
+    W = si.gaussian_weights(4, N, K)
+    packed, gw, t = oracle.pack_weights(W)
+    for j, a in ((0, 0.75), (5, -1.5), (K - 1, 3.0)):
+        x = (np.float32(a) * H[j])[None, :]
+        y = oracle.forward(x, packed, gw, N, bits, True)
+        expect = a * math.sqrt(K) * t[:, j].astype(np.float64) * float(gw)
+        assert np.allclose(y[0], expect, rtol=1e-6, atol=0)
+
+
+def test_forward_is_composition_of_stages():
+    lin = si.workload(1).linears[0]
+    x = si.activations(1, lin)
+    W = si.weights(1, lin)
+    packed, gw, t = oracle.pack_weights(W)
+    y = oracle.forward(x, packed, gw, lin.N, lin.act_bits, lin.use_hadamard)
+    q, s = oracle.quantize(x, lin.act_bits, lin.use_hadamard)
+    y2 = oracle.epilogue(oracle.gemm(q, t), s, gw)
+    assert np.array_equal(y, y2)
+    # the Hadamard spreads the 4 outlier channels: the transformed row is flatter
+    xh = oracle.hadamard(x)
+    kurt = lambda v: np.mean(v ** 4, axis=1) / np.mean(v ** 2, axis=1) ** 2
+    assert np.all(kurt(xh) < kurt(x))
