@@ -1,0 +1,139 @@
+/*
+ * bitnet.h -- C ABI of libbitnet_hip.so: the H-BitLinear forward pass on AMD MI355X (gfx950).
+ *
+ * The layer (BitNet b1.58 / BitNet v2):
+ *   - weights are ternarised offline by absmean and stored five trits per byte, base 3
+ *     [BitNet b1.58 summary of arXiv 2402.17764 (gptget.net), method; BitNet b1.58 2B4T
+ *      write-up (itdecent.cn), section 1.1, worked example (2,0,1,2,1) -> 178];
+ *   - each token's activations optionally go through an online normalised Hadamard transform
+ *     [BitNet v2 news write-up (Xinzhiyuan, kaiyunao.com), H-BitLinear passage; BitNet v2
+ *      abstract (chatpaper.ai)], then are quantised by per-token absmax to INT8 or INT4
+ *     [2B4T write-up section 1.2 (W1.58A8, absmax activations); v2 write-up (4-bit
+ *      activations for all linears)];
+ *   - the product with the ternary weights is integer (add / subtract / skip, int32 sums)
+ *     and is rescaled to fp32 with no bias [2B4T write-up section 1.2; v2 write-up: bias
+ *     removed].
+ *
+ * Conventions (all functions):
+ *   - extern "C", return an int status: BITNET_OK (0) or a negative BITNET_ERR_* code.
+ *   - Shapes: x is M x K fp32 row-major (one token per row); the weight is N x K
+ *     (nn.Linear convention, y = x W^T); out is M x N fp32 row-major.
+ *   - The caller owns every buffer.  The library never allocates or frees device memory and
+ *     keeps no state between calls, so calls are thread-safe.
+ *   - "Device" pointers are HIP device memory on the current device; "host" pointers are
+ *     ordinary CPU memory.  `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *   - Argument checks run on the host before anything is launched; a failing check launches
+ *     nothing and writes nothing.  A HIP launch error maps to BITNET_ERR_HIP.  Device-side
+ *     faults surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Supported shapes: 1 <= M, 1 <= N, 64 <= K <= 65536 with K % 64 == 0; with
+ *     use_hadamard = 1, K must be a power of two, 256 <= K <= 16384.  act_bits is 4 or 8.
+ *     Anything else returns BITNET_ERR_UNSUPPORTED (or BITNET_ERR_SHAPE for sizes <= 0).
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BITNET_OK = 0,
+    BITNET_ERR_NULL = -1,        /* a required pointer is NULL */
+    BITNET_ERR_SHAPE = -2,       /* M, N or K <= 0, or an output buffer is too small */
+    BITNET_ERR_UNSUPPORTED = -3, /* valid but unsupported shape or mode (see above) */
+    BITNET_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the query returned */
+    BITNET_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+    BITNET_ERR_FORMAT = -6       /* a packed weight byte is not a base-3 code (> 242) */
+};
+
+/* Static text for a status code (never NULL). */
+const char *bitnet_status_string(int status);
+
+/* ABI version, currently 1. */
+int bitnet_abi_version(void);
+
+/* ------------------------------------------------------------------------------------ */
+/* Offline weight preparation (host memory, synchronous).                                */
+/* ------------------------------------------------------------------------------------ */
+
+/* Size in bytes of a packed N x K weight: N * 64 * ceil(K / 320).
+ * Packed layout: row n is 64 * ceil(K/320) bytes; byte b of 320-weight block B of that row
+ * holds the weights k = 320 B + b + 64 i (i = 0..4) as base-3 digit i, digit = t + 1, digit 0
+ * the most significant: byte = 81 d0 + 27 d1 + 9 d2 + 3 d3 + d4 (so the digits 2,0,1,2,1 give
+ * 178, the 2B4T write-up's section 1.1 example).  Positions k >= K hold t = 0.
+ * Which five weights share a byte is this library's choice (the pages fix only the byte
+ * code): grouping weights 64 apart lets one 16-byte load decode to five 64-wide MFMA slices. */
+int bitnet_packed_bytes(int N, int K, size_t *bytes_out);
+
+/* absmean ternarisation and packing [gptget.net 2402.17764 summary, method; 2B4T write-up
+ * section 1.1].  W_host: N x K fp32 (host).  gamma = mean |W| (double accumulation, rounded
+ * to fp32 once); t = clamp(round_half_even(W / gamma), -1, 1) with an fp32 division; an
+ * all-zero W gives gamma = 0 and t = 0.  packed_host: bitnet_packed_bytes(N, K) bytes
+ * (host); *w_scale_out receives gamma, the value hbitlinear_forward takes as w_scale. */
+int bitnet_pack_weights(const float *W_host, int N, int K, uint8_t *packed_host,
+                        float *w_scale_out);
+
+/* Inverse of the packing: trits_host (N x K int8, host) receives t in {-1, 0, +1}.
+ * Returns BITNET_ERR_FORMAT if a byte is > 242 or a padding position is not t = 0. */
+int bitnet_unpack_weights(const uint8_t *packed_host, int N, int K, int8_t *trits_host);
+
+/* ------------------------------------------------------------------------------------ */
+/* Forward pass (device memory, asynchronous on `stream`).                               */
+/* ------------------------------------------------------------------------------------ */
+
+/* Bytes of device workspace hbitlinear_forward needs for M tokens of width K:
+ * the activation codes (hbitlinear_codes_bytes) and M fp32 scales, each 256-byte aligned. */
+int hbitlinear_workspace_bytes(int M, int K, int act_bits, size_t *bytes_out);
+
+/* H-BitLinear (use_hadamard = 1) or BitLinear (use_hadamard = 0) forward:
+ *   x_h = use_hadamard ? x H_K / sqrt(K) : x                (per token, Sylvester H_K)
+ *   q, s = per-token absmax quantisation of x_h to act_bits  (Qp = 2^(b-1) - 1)
+ *   out[m][n] = (float(sum_k q[m][k] t[n][k]) * s[m]) * w_scale
+ * x (M x K fp32), out (M x N fp32), packed_w (bitnet_packed_bytes(N, K) bytes) and workspace
+ * are device pointers; w_scale is the gamma returned by bitnet_pack_weights.  Equal to
+ * hbitlinear_quantize into the workspace followed by hbitlinear_gemm_dequant. */
+int hbitlinear_forward(const float *x, int M, int K, int N, int act_bits, int use_hadamard,
+                       float *out, const uint8_t *packed_w, float w_scale, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* The two stages of the forward, exported so each can be checked and timed on its own.  */
+/* ------------------------------------------------------------------------------------ */
+
+/* Size of the activation codes of M x K: M*K bytes (INT8) or M*K/2 bytes (INT4). */
+int hbitlinear_codes_bytes(int M, int K, int act_bits, size_t *bytes_out);
+
+/* Activation stage [v2 write-up H-BitLinear passage; 2B4T write-up section 1.2]: optional
+ * normalised Hadamard (radix-2 stages with span 1, 2, 4, ..., K/2, then one fp32 multiply by
+ * (float)(1/sqrt(K))), then per-token absmax quantisation:
+ *   gamma = max_k |x_h[k]|;  q = clamp(round_half_even(x_h * (Qp / gamma)), -Qp-1, Qp);
+ *   s = gamma / Qp;  a zero row gives q = 0, s = 0.
+ * codes (device): INT8 -> M x K int8; INT4 -> M x K/2 bytes: the codes k = 8w .. 8w+7 of a row
+ * live in its 4-byte word w, byte p (0..3) holding code 8w+p in the low nibble and code
+ * 8w+p+4 in the high nibble (two's complement), so a word unpacks to two int8 words in k
+ * order with one mask and one shift.  scales (device): M fp32.  xh_or_null (device, M x K
+ * fp32, may be NULL) receives x_h. */
+int hbitlinear_quantize(const float *x, int M, int K, int act_bits, int use_hadamard,
+                        uint8_t *codes, float *scales, float *xh_or_null, void *stream);
+
+/* Ternary product [2B4T write-up section 1.2]: acc[m][n] = sum_k q[m][k] t[n][k], exact
+ * int32.  codes as written by hbitlinear_quantize; packed_w as bitnet_pack_weights; acc is
+ * M x N int32 (device). */
+int bitnet_ternary_gemm_i32(const uint8_t *codes, int M, int K, int N, int act_bits,
+                            const uint8_t *packed_w, int32_t *acc, void *stream);
+
+/* Ternary product fused with the dequantisation epilogue (no bias [v2 write-up]):
+ * out[m][n] = (float(acc[m][n]) * scales[m]) * w_scale, fp32, left to right.  All pointers
+ * device. */
+int hbitlinear_gemm_dequant(const uint8_t *codes, const float *scales, int M, int K, int N,
+                            int act_bits, const uint8_t *packed_w, float w_scale, float *out,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

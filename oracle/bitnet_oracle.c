@@ -217,21 +217,25 @@ void bitnet_ref_quantize_row(const float *x, int K, int bits, int8_t *q, float *
     *scale_out = g / (float)qp;
 }
 
-/* INT4 codes two to a byte: low nibble holds the even k, high nibble the odd k (two's       */
-/* complement nibbles).  The pages say only that activations are 4-bit.                     */
+/* INT4 codes two to a byte.  The pages say only that activations are 4-bit; the nibble order  */
+/* taken here: codes are grouped in eights, k = 8w .. 8w+7, stored in the 4-byte word w of the */
+/* row; byte p (p = 0..3) of that word holds code 8w+p in its low nibble and code 8w+p+4 in   */
+/* its high nibble (two's complement nibbles).  count must be a multiple of 8.               */
 void bitnet_ref_pack_int4(const int8_t *q, int64_t count, uint8_t *out)
 {
-    for (int64_t i = 0; i < count / 2; i++)
-        out[i] = (uint8_t)((q[2 * i] & 0xF) | ((q[2 * i + 1] & 0xF) << 4));
+    for (int64_t w = 0; w < count / 8; w++)
+        for (int p = 0; p < 4; p++)
+            out[4 * w + p] = (uint8_t)((q[8 * w + p] & 0xF) | ((q[8 * w + p + 4] & 0xF) << 4));
 }
 
 void bitnet_ref_unpack_int4(const uint8_t *in, int64_t count, int8_t *q)
 {
-    for (int64_t i = 0; i < count / 2; i++) {
-        int lo = in[i] & 0xF, hi = in[i] >> 4;
-        q[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
-        q[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
-    }
+    for (int64_t w = 0; w < count / 8; w++)
+        for (int p = 0; p < 4; p++) {
+            int lo = in[4 * w + p] & 0xF, hi = in[4 * w + p] >> 4;
+            q[8 * w + p] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+            q[8 * w + p + 4] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+        }
 }
 
 /* Activation stage of H-BitLinear for M token rows: optional normalised Hadamard, then      */

@@ -257,10 +257,14 @@ def test_quantize_zero_row_and_sign_symmetry():
 
 
 def test_int4_nibble_layout():
-    q = np.array([[1, -1, 7, -8, 0, 3]], np.int8)
+    q = np.array([[1, -1, 7, -8, 0, 3, -2, 5]], np.int8)
     b = oracle.pack_int4(q)
-    assert list(b[0]) == [0xF1, 0x87, 0x30]
-    assert np.array_equal(oracle.unpack_int4(b, 6), q)
+    # byte p holds code p (low nibble) and code p + 4 (high nibble)
+    assert list(b[0]) == [0x01, 0x3F, 0xE7, 0x58]
+    assert np.array_equal(oracle.unpack_int4(b, 8), q)
+    rng = np.random.default_rng(3)
+    q2 = rng.integers(-8, 8, size=(3, 64)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(q2), 64), q2)
 
 
 # ------------------------------------------------------------------- ternary product ----
