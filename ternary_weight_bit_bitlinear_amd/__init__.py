@@ -1,0 +1,13 @@
+"""H-BitLinear (BitNet b1.58 / BitNet v2) forward pass for AMD MI355X (gfx950).
+
+The compute lives in ``libbitnet_hip.so`` (hand-written HIP kernels behind the C ABI of
+``include/bitnet.h``); :mod:`.bitnet` is its Python binding.  Build the library with
+``python -m ternary_weight_bit_bitlinear_amd.build``.
+"""
+from .bitnet import (  # noqa: F401
+    BITNET_ERR_FORMAT, BITNET_ERR_HIP, BITNET_ERR_NULL, BITNET_ERR_SHAPE,
+    BITNET_ERR_UNSUPPORTED, BITNET_ERR_WORKSPACE, BITNET_OK, BitnetError, LIB_PATH,
+    bitnet_abi_version, bitnet_pack_weights, bitnet_packed_bytes, bitnet_status_string,
+    bitnet_ternary_gemm_i32, bitnet_unpack_weights, hbitlinear_codes_bytes, hbitlinear_forward,
+    hbitlinear_gemm_dequant, hbitlinear_quantize, hbitlinear_workspace_bytes, lib,
+)

@@ -1,0 +1,225 @@
+"""Python binding of libbitnet_hip.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/bitnet.h).  Device buffers
+are torch CUDA (HIP) tensors; PyTorch supplies the memory and the stream, and every step of
+the forward runs in the library's HIP kernels.  There is no fallback: if the library is not
+built, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitnet_hip.so")
+
+BITNET_OK = 0
+BITNET_ERR_NULL = -1
+BITNET_ERR_SHAPE = -2
+BITNET_ERR_UNSUPPORTED = -3
+BITNET_ERR_WORKSPACE = -4
+BITNET_ERR_HIP = -5
+BITNET_ERR_FORMAT = -6
+
+_lib = None
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bitnet_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m ternary_weight_bit_bitlinear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        PSZ = ctypes.POINTER(ctypes.c_size_t)
+        sigs = {
+            "bitnet_status_string": ([I], ctypes.c_char_p),
+            "bitnet_abi_version": ([], I),
+            "bitnet_packed_bytes": ([I, I, PSZ], I),
+            "bitnet_pack_weights": ([P, I, I, P, P], I),
+            "bitnet_unpack_weights": ([P, I, I, P], I),
+            "hbitlinear_workspace_bytes": ([I, I, I, PSZ], I),
+            "hbitlinear_codes_bytes": ([I, I, I, PSZ], I),
+            "hbitlinear_forward": ([P, I, I, I, I, I, P, P, F, P, SZ, P], I),
+            "hbitlinear_quantize": ([P, I, I, I, I, P, P, P, P], I),
+            "bitnet_ternary_gemm_i32": ([P, I, I, I, I, P, P, P], I),
+            "hbitlinear_gemm_dequant": ([P, P, I, I, I, I, P, F, P, P], I),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != BITNET_OK:
+        raise BitnetError(status, where)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(None)
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return ctypes.c_void_p(t.ctypes.data)
+    assert t.is_contiguous(), "tensor must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_check(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---- status / sizes -------------------------------------------------------------------------
+
+def bitnet_status_string(status: int) -> str:
+    return lib().bitnet_status_string(int(status)).decode()
+
+
+def bitnet_abi_version() -> int:
+    return int(lib().bitnet_abi_version())
+
+
+def bitnet_packed_bytes(N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().bitnet_packed_bytes(N, K, ctypes.byref(out)), "bitnet_packed_bytes")
+    return int(out.value)
+
+
+def hbitlinear_workspace_bytes(M: int, K: int, act_bits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().hbitlinear_workspace_bytes(M, K, act_bits, ctypes.byref(out)),
+           "hbitlinear_workspace_bytes")
+    return int(out.value)
+
+
+def hbitlinear_codes_bytes(M: int, K: int, act_bits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().hbitlinear_codes_bytes(M, K, act_bits, ctypes.byref(out)), "hbitlinear_codes_bytes")
+    return int(out.value)
+
+
+# ---- offline weights (host) -----------------------------------------------------------------
+
+def bitnet_pack_weights(W):
+    """absmean-ternarise and pack an N x K fp32 host matrix -> (packed uint8, w_scale float)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    packed = np.empty(bitnet_packed_bytes(N, K), np.uint8)
+    g = ctypes.c_float(0.0)
+    _check(lib().bitnet_pack_weights(_ptr(W), N, K, _ptr(packed), ctypes.byref(g)),
+           "bitnet_pack_weights")
+    return packed, float(g.value)
+
+
+def bitnet_unpack_weights(packed, N: int, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    t = np.empty((N, K), np.int8)
+    _check(lib().bitnet_unpack_weights(_ptr(packed), N, K, _ptr(t)), "bitnet_unpack_weights")
+    return t
+
+
+# ---- forward (device) -----------------------------------------------------------------------
+
+def hbitlinear_forward(x, N: int, act_bits: int, use_hadamard: bool, packed_w, w_scale: float,
+                       out=None, workspace=None, stream=None):
+    """out = H-BitLinear(x) for x (M x K fp32, device); returns out (M x N fp32, device)."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * N:
+        raise ValueError("out is too small")
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_workspace_bytes(M, K, act_bits), dtype=torch.uint8,
+                                device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward(_ptr(x), M, K, N, act_bits, int(bool(use_hadamard)),
+                                    _ptr(out), _ptr(packed_w), float(w_scale), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "hbitlinear_forward")
+    return out
+
+
+def hbitlinear_quantize(x, act_bits: int, use_hadamard: bool, codes=None, scales=None,
+                        want_xh: bool = False, stream=None):
+    """Activation stage -> (codes uint8, scales fp32[, xh fp32]) on the device."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty(hbitlinear_codes_bytes(M, K, act_bits), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    xh = torch.empty((M, K), dtype=torch.float32, device=x.device) if want_xh else None
+    _check(lib().hbitlinear_quantize(_ptr(x), M, K, act_bits, int(bool(use_hadamard)), _ptr(codes),
+                                     _ptr(scales), _ptr(xh), _stream(stream)), "hbitlinear_quantize")
+    return (codes, scales, xh) if want_xh else (codes, scales)
+
+
+def bitnet_ternary_gemm_i32(codes, M: int, K: int, N: int, act_bits: int, packed_w, acc=None,
+                            stream=None):
+    """acc = sum_k q t (exact int32, M x N, device) from device codes and packed weights."""
+    import torch
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits):
+        raise ValueError("codes buffer is too small")
+    if packed_w.numel() < bitnet_packed_bytes(N, K):
+        raise ValueError("packed_w buffer is too small")
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    _dev_check(acc, torch.int32, "acc")
+    _check(lib().bitnet_ternary_gemm_i32(_ptr(codes), M, K, N, act_bits, _ptr(packed_w), _ptr(acc),
+                                         _stream(stream)), "bitnet_ternary_gemm_i32")
+    return acc
+
+
+def hbitlinear_gemm_dequant(codes, scales, M: int, K: int, N: int, act_bits: int, packed_w,
+                            w_scale: float, out=None, stream=None):
+    import torch
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    if packed_w.numel() < bitnet_packed_bytes(N, K):
+        raise ValueError("packed_w buffer is too small")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _dev_check(out, torch.float32, "out")
+    _check(lib().hbitlinear_gemm_dequant(_ptr(codes), _ptr(scales), M, K, N, act_bits,
+                                         _ptr(packed_w), float(w_scale), _ptr(out),
+                                         _stream(stream)), "hbitlinear_gemm_dequant")
+    return out

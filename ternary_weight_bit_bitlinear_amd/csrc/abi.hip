@@ -1,0 +1,119 @@
+// abi.hip -- the extern "C" entry points of libbitnet_hip.so (declared in include/bitnet.h).
+// Every entry point checks its arguments on the host first and launches nothing when a check
+// fails; work is queued on the caller's stream.
+#include "common.h"
+
+using namespace bitnet;
+
+namespace {
+
+int check_shape(int M, int K, int N, int bits, int use_hadamard)
+{
+    if (M <= 0 || K <= 0 || N <= 0) return BITNET_ERR_SHAPE;
+    if (bits != 4 && bits != 8) return BITNET_ERR_UNSUPPORTED;
+    if (use_hadamard != 0 && use_hadamard != 1) return BITNET_ERR_UNSUPPORTED;
+    if (K % 64 != 0 || K > 65536) return BITNET_ERR_UNSUPPORTED;
+    if (use_hadamard) {
+        if ((K & (K - 1)) != 0 || K < 256 || K > 16384) return BITNET_ERR_UNSUPPORTED;
+    }
+    if ((int64_t)M > (int64_t)65535 * 256) return BITNET_ERR_UNSUPPORTED;  // grid limit
+    return BITNET_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_HIP; }
+
+size_t codes_bytes(int M, int K, int bits) { return (size_t)M * (size_t)codes_row_bytes(K, bits); }
+
+size_t workspace_bytes(int M, int K, int bits)
+{
+    return align256(codes_bytes(M, K, bits)) + align256((size_t)M * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitnet_status_string(int status)
+{
+    switch (status) {
+    case BITNET_OK: return "ok";
+    case BITNET_ERR_NULL: return "a required pointer is NULL";
+    case BITNET_ERR_SHAPE: return "invalid size (M, N or K <= 0, or buffer too small)";
+    case BITNET_ERR_UNSUPPORTED: return "unsupported shape or mode";
+    case BITNET_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITNET_ERR_HIP: return "HIP runtime or launch error";
+    case BITNET_ERR_FORMAT: return "packed weight byte is not a base-3 code";
+    default: return "unknown status";
+    }
+}
+
+int bitnet_abi_version(void) { return 1; }
+
+int hbitlinear_codes_bytes(int M, int K, int act_bits, size_t* bytes_out)
+{
+    if (bytes_out == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, 1, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    *bytes_out = codes_bytes(M, K, act_bits);
+    return BITNET_OK;
+}
+
+int hbitlinear_workspace_bytes(int M, int K, int act_bits, size_t* bytes_out)
+{
+    if (bytes_out == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, 1, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    *bytes_out = workspace_bytes(M, K, act_bits);
+    return BITNET_OK;
+}
+
+int hbitlinear_quantize(const float* x, int M, int K, int act_bits, int use_hadamard,
+                        uint8_t* codes, float* scales, float* xh_or_null, void* stream)
+{
+    if (x == nullptr || codes == nullptr || scales == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, 1, act_bits, use_hadamard);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, xh_or_null,
+                                     (hipStream_t)stream));
+}
+
+int bitnet_ternary_gemm_i32(const uint8_t* codes, int M, int K, int N, int act_bits,
+                            const uint8_t* packed_w, int32_t* acc, void* stream)
+{
+    if (codes == nullptr || packed_w == nullptr || acc == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, nullptr, 0.0f, nullptr, acc,
+                                 (hipStream_t)stream));
+}
+
+int hbitlinear_gemm_dequant(const uint8_t* codes, const float* scales, int M, int K, int N,
+                            int act_bits, const uint8_t* packed_w, float w_scale, float* out,
+                            void* stream)
+{
+    if (codes == nullptr || scales == nullptr || packed_w == nullptr || out == nullptr)
+        return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, scales, w_scale, out, nullptr,
+                                 (hipStream_t)stream));
+}
+
+int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int use_hadamard,
+                       float* out, const uint8_t* packed_w, float w_scale, void* workspace,
+                       size_t workspace_size, void* stream)
+{
+    if (x == nullptr || out == nullptr || packed_w == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc != BITNET_OK) return rc;
+    if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, scales, w_scale, out, nullptr, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// common.h -- internal helpers shared by the kernels and the C ABI of libbitnet_hip.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bitnet.h"
+
+namespace bitnet {
+
+// Packed weight geometry: a row is cut into blocks of 320 weights stored in 64 bytes; byte b
+// of block B holds the weights k = 320 B + b + 64 i, i = 0..4, as base-3 digit i (MSB first).
+constexpr int kBlockWeights = 320;
+constexpr int kBlockBytes = 64;
+constexpr int kSlab = 64;  // weights per digit slab of a block (one MFMA k-extent)
+
+inline int64_t row_bytes(int K) { return (int64_t)kBlockBytes * ((K + kBlockWeights - 1) / kBlockWeights); }
+
+inline int64_t codes_row_bytes(int K, int bits) { return bits == 8 ? (int64_t)K : (int64_t)K / 2; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Internal launchers (quant.hip, gemm.hip).  Arguments are validated by the caller.
+hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
+                           uint8_t* codes, float* scales, float* xh, hipStream_t stream);
+
+// out_f32 != nullptr: out = (float(acc) * scales[m]) * w_scale;  else acc_i32 receives acc.
+hipError_t launch_gemm(const uint8_t* codes, int M, int K, int N, int bits,
+                       const uint8_t* packed, const float* scales, float w_scale,
+                       float* out_f32, int32_t* acc_i32, hipStream_t stream);
+
+}  // namespace bitnet

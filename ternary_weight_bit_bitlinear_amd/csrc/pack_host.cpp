@@ -1,0 +1,113 @@
+// pack_host.cpp -- offline weight preparation of libbitnet_hip.so (host code).
+//
+// absmean ternarisation [BitNet b1.58 summary of arXiv 2402.17764 (gptget.net), method: weights
+// constrained to {-1, 0, +1} by the absmean function] and base-3 packing, five trits per byte
+// [BitNet b1.58 2B4T write-up (itdecent.cn), section 1.1: a byte holds five ternary digits,
+// most significant first -- the digits 2,0,1,2,1 give 178].
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/bitnet.h"
+
+namespace {
+
+constexpr int kBlock = 320;  // weights per 64-byte block of a packed row
+
+int64_t packed_row_bytes(int K) { return 64 * (int64_t)((K + kBlock - 1) / kBlock); }
+
+int check_nk(int N, int K)
+{
+    if (N <= 0 || K <= 0) return BITNET_ERR_SHAPE;
+    if ((int64_t)N * (int64_t)K > ((int64_t)1 << 40)) return BITNET_ERR_UNSUPPORTED;
+    return BITNET_OK;
+}
+
+// One trit in {-1, 0, +1}: round-half-to-even of an fp32 quotient, clipped.
+inline int ternary(float w, float gamma)
+{
+    float r = std::nearbyint(w / gamma);
+    return r >= 1.0f ? 1 : (r <= -1.0f ? -1 : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_packed_bytes(int N, int K, size_t* bytes_out)
+{
+    if (bytes_out == nullptr) return BITNET_ERR_NULL;
+    int rc = check_nk(N, K);
+    if (rc != BITNET_OK) return rc;
+    *bytes_out = (size_t)N * (size_t)packed_row_bytes(K);
+    return BITNET_OK;
+}
+
+int bitnet_pack_weights(const float* W, int N, int K, uint8_t* packed, float* w_scale_out)
+{
+    if (W == nullptr || packed == nullptr || w_scale_out == nullptr) return BITNET_ERR_NULL;
+    int rc = check_nk(N, K);
+    if (rc != BITNET_OK) return rc;
+    const int64_t count = (int64_t)N * K;
+    // gamma = mean |W|: one double sum over the matrix in row-major order, rounded once.
+    double sum = 0.0;
+    for (int64_t i = 0; i < count; i++) sum += std::fabs((double)W[i]);
+    const float gamma = (float)(sum / (double)count);
+    *w_scale_out = gamma;
+
+    const int64_t rb = packed_row_bytes(K);
+    const int nblk = (K + kBlock - 1) / kBlock;
+    for (int n = 0; n < N; n++) {
+        const float* wr = W + (int64_t)n * K;
+        uint8_t* pr = packed + (int64_t)n * rb;
+        for (int blk = 0; blk < nblk; blk++) {
+            for (int b = 0; b < 64; b++) {
+                // byte b of the block: weights k = 320 blk + b + 64 i as digit i, MSB first
+                int v = 0;
+                for (int i = 0; i < 5; i++) {
+                    const int k = kBlock * blk + b + 64 * i;
+                    const int t = (k < K && gamma != 0.0f) ? ternary(wr[k], gamma) : 0;
+                    v = 3 * v + (t + 1);
+                }
+                pr[64 * blk + b] = (uint8_t)v;
+            }
+        }
+    }
+    return BITNET_OK;
+}
+
+int bitnet_unpack_weights(const uint8_t* packed, int N, int K, int8_t* trits)
+{
+    if (packed == nullptr || trits == nullptr) return BITNET_ERR_NULL;
+    int rc = check_nk(N, K);
+    if (rc != BITNET_OK) return rc;
+    const int64_t rb = packed_row_bytes(K);
+    const int nblk = (K + kBlock - 1) / kBlock;
+    // Two passes: check every byte first, so a malformed buffer leaves trits untouched.
+    for (int pass = 0; pass < 2; pass++) {
+        for (int n = 0; n < N; n++) {
+            const uint8_t* pr = packed + (int64_t)n * rb;
+            int8_t* tr = trits + (int64_t)n * K;
+            for (int blk = 0; blk < nblk; blk++) {
+                for (int b = 0; b < 64; b++) {
+                    int v = pr[64 * blk + b];
+                    if (v > 242) return BITNET_ERR_FORMAT;
+                    for (int i = 4; i >= 0; i--) {  // least significant digit is i = 4
+                        const int d = v % 3;
+                        v /= 3;
+                        const int k = kBlock * blk + b + 64 * i;
+                        if (k >= K) {
+                            if (d != 1) return BITNET_ERR_FORMAT;
+                        } else if (pass == 1) {
+                            tr[k] = (int8_t)(d - 1);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    return BITNET_OK;
+}
+
+}  // extern "C"

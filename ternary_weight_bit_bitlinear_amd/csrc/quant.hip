@@ -1,0 +1,370 @@
+// quant.hip -- activation stage of H-BitLinear on gfx950: online normalised Hadamard transform,
+// per-token absmax, quantisation to INT8 / INT4 codes.  One workgroup per token row.
+//
+// Method: BitNet v2 news write-up (Xinzhiyuan), H-BitLinear passage -- an online Hadamard
+// transform (entries +1/-1, orthogonal rows) applied before activation quantisation; BitNet
+// b1.58 2B4T write-up (itdecent.cn), section 1.2 -- absmax activation quantisation.
+//
+// The transform is the Sylvester H_K / sqrt(K).  Its radix-2 stages run with butterfly span
+// 1, 2, 4, ..., K/2 (index bit 0 first), each butterfly (a, b) -> (a + b, a - b), and the
+// 1/sqrt(K) is one fp32 multiply after the last stage.  Every thread keeps E = K/T values of
+// the row in registers.  The stages are grouped: a group handles the index bits that are
+// register bits in the current data layout; between groups the row is exchanged through LDS
+// into the next layout.  Whatever the grouping, every element is formed from the same
+// operands in the same stage order as the plain in-place butterfly, so the fp32 results do
+// not depend on the grouping.
+//
+// Layouts (K = 2^L, T threads, E = K/T = 2^LE):
+//   load layout A: thread t, register e = 4 r + j holds k = r*4T + 4t + j (float4 loads,
+//                  fully coalesced); its register bits are {0, 1} and the top LE-2 bits.
+//   group p >= 1:  register bits are the next LE not-yet-transformed index bits, padded with
+//                  the lowest bits when fewer remain; the other bits index the thread.
+// LDS addresses are XOR-swizzled, addr(k) = k ^ (((k >> 8) & 7) << 2): it keeps 16-byte
+// chunks whole and spreads the strided accesses of the middle group over the banks.
+#include "common.h"
+
+namespace bitnet {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ constexpr int threads_for(int L) { return L >= 12 ? (1 << (L - 6)) : 64; }
+__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v >> 1); }
+
+// Deposit the low bits of v into the set bits of mask, lowest first.
+__host__ __device__ constexpr uint32_t pdep(uint32_t v, uint32_t mask)
+{
+    uint32_t r = 0;
+    for (int b = 0; b < 32; b++) {
+        if (mask & (1u << b)) {
+            if (v & 1u) r |= 1u << b;
+            v >>= 1;
+        }
+    }
+    return r;
+}
+
+// Register-bit mask of group p (p = 0 is the load layout).
+__host__ __device__ constexpr uint32_t group_mask(int L, int LE, int p)
+{
+    if (p == 0) {
+        int LT = L - LE;
+        uint32_t hi = ((1u << (LE - 2)) - 1u) << (2 + LT);
+        return 3u | hi;
+    }
+    int lo = 2 + (p - 1) * LE;
+    int hi = lo + LE < L ? lo + LE : L;
+    uint32_t m = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+    int pad = LE - (hi - lo);
+    return m | ((1u << pad) - 1u);
+}
+
+__host__ __device__ constexpr int num_groups(int L, int LE) { return 1 + (L - 2 + LE - 1) / LE; }
+
+__device__ __forceinline__ uint32_t swz(uint32_t k) { return k ^ (((k >> 8) & 7u) << 2); }
+
+// Position of index bit b among the register bits of MASK.
+__host__ __device__ constexpr int regpos(uint32_t mask, int b)
+{
+    int pos = 0;
+    for (int c = 0; c < b; c++)
+        if (mask & (1u << c)) pos++;
+    return pos;
+}
+
+// Stage of index bit B: butterflies between registers whose indices differ in regpos(MASK, B).
+template <int E, uint32_t MASK, int B>
+__device__ __forceinline__ void stage(float (&v)[E])
+{
+    constexpr int h = 1 << regpos(MASK, B);
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        if ((e & h) == 0) {
+            float a = v[e], b = v[e + h];
+            v[e] = a + b;
+            v[e + h] = a - b;
+        }
+    }
+}
+
+// Stages for index bits LO, LO+1, ..., HI-1, in that order.
+template <int E, uint32_t MASK, int LO, int HI>
+__device__ __forceinline__ void butterflies(float (&v)[E])
+{
+    if constexpr (LO < HI) {
+        stage<E, MASK, LO>(v);
+        butterflies<E, MASK, LO + 1, HI>(v);
+    }
+}
+
+template <int L>
+struct Geometry {
+    static constexpr int K = 1 << L;
+    static constexpr int T = threads_for(L);
+    static constexpr int LT = ilog2c(T);
+    static constexpr int LE = L - LT;
+    static constexpr int E = 1 << LE;
+    static constexpr int G = num_groups(L, LE);
+};
+
+// Thread part of k in a layout with register mask MASK.
+template <int L, uint32_t MASK>
+__device__ __forceinline__ uint32_t thread_bits(uint32_t t)
+{
+    return pdep(t, ((1u << L) - 1u) & ~MASK);
+}
+
+template <int L, uint32_t MASK, int E>
+__device__ __forceinline__ void store_layout(float* lds, uint32_t t, const float (&v)[E])
+{
+    const uint32_t tb = thread_bits<L, MASK>(t);
+    if constexpr ((MASK & 3u) == 3u) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            uint32_t k = tb | pdep((uint32_t)e, MASK);
+            *reinterpret_cast<float4*>(lds + swz(k)) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; e++) lds[swz(tb | pdep((uint32_t)e, MASK))] = v[e];
+    }
+}
+
+template <int L, uint32_t MASK, int E>
+__device__ __forceinline__ void load_layout(const float* lds, uint32_t t, float (&v)[E])
+{
+    const uint32_t tb = thread_bits<L, MASK>(t);
+    if constexpr ((MASK & 3u) == 3u) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            uint32_t k = tb | pdep((uint32_t)e, MASK);
+            float4 f = *reinterpret_cast<const float4*>(lds + swz(k));
+            v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; e++) v[e] = lds[swz(tb | pdep((uint32_t)e, MASK))];
+    }
+}
+
+// Groups 1.. of the transform, recursively (each step: LDS exchange, then its stages).
+template <int L, int P>
+__device__ __forceinline__ void transform_groups(float* lds, uint32_t t,
+                                                 float (&v)[Geometry<L>::E])
+{
+    using G = Geometry<L>;
+    if constexpr (P < G::G) {
+        constexpr uint32_t PREV = group_mask(L, G::LE, P - 1);
+        constexpr uint32_t CUR = group_mask(L, G::LE, P);
+        constexpr int LO = 2 + (P - 1) * G::LE;
+        constexpr int HI = LO + G::LE < L ? LO + G::LE : L;
+        store_layout<L, PREV, G::E>(lds, t, v);
+        __syncthreads();
+        load_layout<L, CUR, G::E>(lds, t, v);
+        __syncthreads();
+        butterflies<G::E, CUR, LO, HI>(v);
+        transform_groups<L, P + 1>(lds, t, v);
+    }
+}
+
+template <int L, bool HAD>
+__device__ __forceinline__ constexpr uint32_t final_mask()
+{
+    using G = Geometry<L>;
+    return HAD ? group_mask(L, G::LE, G::G - 1) : group_mask(L, G::LE, 0);
+}
+
+template <int BITS>
+__device__ __forceinline__ int quant_code(float x, float inv)
+{
+    constexpr int QP = (1 << (BITS - 1)) - 1;
+    float r = __builtin_rintf(x * inv);        // round half to even (v_rndne_f32)
+    int q = (int)r;
+    q = q > QP ? QP : q;
+    q = q < -QP - 1 ? -QP - 1 : q;
+    return q;
+}
+
+template <int L, int BITS, bool HAD>
+__global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
+    const float* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    float* __restrict__ xh, float hadamard_c)
+{
+    using G = Geometry<L>;
+    constexpr int K = G::K, T = G::T, E = G::E;
+    constexpr int QP = (1 << (BITS - 1)) - 1;
+    __shared__ __align__(16) float lds[K];
+    // Reduction slots sit past the K code bytes that are written after the reduction.
+    float* red = lds + K / 2;
+
+    const uint32_t t = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const float* xr = x + m * K;
+
+    // Load layout A: coalesced float4 loads.
+    float v[E];
+#pragma unroll
+    for (int r = 0; r < E / 4; r++) {
+        f4 f = __builtin_nontemporal_load(reinterpret_cast<const f4*>(xr) + r * T + t);
+        v[4 * r] = f[0]; v[4 * r + 1] = f[1]; v[4 * r + 2] = f[2]; v[4 * r + 3] = f[3];
+    }
+
+    if constexpr (HAD) {
+        butterflies<E, group_mask(L, G::LE, 0), 0, 2>(v);
+        transform_groups<L, 1>(lds, t, v);
+#pragma unroll
+        for (int e = 0; e < E; e++) v[e] = v[e] * hadamard_c;
+    }
+    constexpr uint32_t FM = final_mask<L, HAD>();
+    const uint32_t tb = thread_bits<L, FM>(t);
+
+    if (xh != nullptr) {
+        float* xo = xh + m * K;
+#pragma unroll
+        for (int e = 0; e < E; e++) xo[tb | pdep((uint32_t)e, FM)] = v[e];
+    }
+
+    // absmax over the row: exact, so the reduction order does not matter.
+    float g = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; e++) g = fmaxf(g, fabsf(v[e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = g;
+    __syncthreads();
+    g = red[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; w++) g = fmaxf(g, red[w]);
+
+    const float inv = g > 0.0f ? (float)QP / g : 0.0f;   // IEEE division
+    if (t == 0) scales[m] = g > 0.0f ? g / (float)QP : 0.0f;
+
+    // Codes into LDS as bytes at position k, then out with 16-byte stores.
+    int8_t* qb = reinterpret_cast<int8_t*>(lds);
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        int q = g > 0.0f ? quant_code<BITS>(v[e], inv) : 0;
+        qb[tb | pdep((uint32_t)e, FM)] = (int8_t)q;
+    }
+    __syncthreads();
+    if constexpr (BITS == 8) {
+        uint4* dst = reinterpret_cast<uint4*>(codes + m * K);
+        const uint4* src = reinterpret_cast<const uint4*>(qb);
+        for (int c = t; c < K / 16; c += T) dst[c] = src[c];
+    } else {
+        // 32 codes -> 16 bytes: word w holds codes 8w+p (low nibble) and 8w+p+4 (high nibble).
+        uint4* dst = reinterpret_cast<uint4*>(codes + m * (K / 2));
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(qb);
+        for (int c = t; c < K / 32; c += T) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t lo = src[8 * c + 2 * i], hi = src[8 * c + 2 * i + 1];
+                w[i] = (lo & 0x0F0F0F0Fu) | ((hi & 0x0F0F0F0Fu) << 4);
+            }
+            dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// Rows whose width is not a power of two in [256, 16384] (no Hadamard): two passes over the row.
+template <int BITS>
+__global__ __launch_bounds__(256) void quantize_rows_generic_kernel(
+    const float* __restrict__ x, int K, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    float* __restrict__ xh)
+{
+    constexpr int QP = (1 << (BITS - 1)) - 1;
+    __shared__ float red[4];
+    const int t = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + m * K);
+    const int nc = K / 4;
+    float g = 0.0f;
+    for (int c = t; c < nc; c += 256) {
+        float4 f = xr[c];
+        g = fmaxf(g, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = g;
+    __syncthreads();
+    g = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = g > 0.0f ? (float)QP / g : 0.0f;
+    if (t == 0) scales[m] = g > 0.0f ? g / (float)QP : 0.0f;
+    if (xh != nullptr) {
+        float4* xo = reinterpret_cast<float4*>(xh + m * K);
+        for (int c = t; c < nc; c += 256) xo[c] = xr[c];
+    }
+    // 8 codes per step (two float4): keeps INT4 words whole.
+    for (int c2 = t; c2 < nc / 2; c2 += 256) {
+        float4 a = xr[2 * c2], b = xr[2 * c2 + 1];
+        float vals[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) q[i] = g > 0.0f ? quant_code<BITS>(vals[i], inv) : 0;
+        if constexpr (BITS == 8) {
+            uint32_t lo = (q[0] & 255) | (q[1] & 255) << 8 | (q[2] & 255) << 16 | (uint32_t)(q[3] & 255) << 24;
+            uint32_t hi = (q[4] & 255) | (q[5] & 255) << 8 | (q[6] & 255) << 16 | (uint32_t)(q[7] & 255) << 24;
+            reinterpret_cast<uint2*>(codes + m * K)[c2] = make_uint2(lo, hi);
+        } else {
+            uint32_t w = 0;
+#pragma unroll
+            for (int p = 0; p < 4; p++) w |= (uint32_t)((q[p] & 15) | ((q[p + 4] & 15) << 4)) << (8 * p);
+            reinterpret_cast<uint32_t*>(codes + m * (K / 2))[c2] = w;
+        }
+    }
+}
+
+template <int L, int BITS, bool HAD>
+hipError_t launch_rows(const float* x, int M, uint8_t* codes, float* scales, float* xh, float c,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD>), dim3(M), dim3(Geometry<L>::T), 0, s,
+                       x, codes, scales, xh, c);
+    return hipGetLastError();
+}
+
+template <int BITS, bool HAD>
+hipError_t dispatch_L(int L, const float* x, int M, uint8_t* codes, float* scales, float* xh,
+                      float c, hipStream_t s)
+{
+    switch (L) {
+    case 8: return launch_rows<8, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 9: return launch_rows<9, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 10: return launch_rows<10, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 11: return launch_rows<11, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 12: return launch_rows<12, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 13: return launch_rows<13, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 14: return launch_rows<14, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
+                           uint8_t* codes, float* scales, float* xh, hipStream_t stream)
+{
+    int L = 0;
+    while ((1 << L) < K) L++;
+    const bool pow2 = (1 << L) == K && L >= 8 && L <= 14;
+    // 1/sqrt(K) rounded once to fp32 from a correctly rounded double square root.
+    const float c = (float)(1.0 / __builtin_sqrt((double)K));
+    if (use_hadamard) {
+        if (!pow2) return hipErrorInvalidValue;
+        return bits == 8 ? dispatch_L<8, true>(L, x, M, codes, scales, xh, c, stream)
+                         : dispatch_L<4, true>(L, x, M, codes, scales, xh, c, stream);
+    }
+    if (pow2)
+        return bits == 8 ? dispatch_L<8, false>(L, x, M, codes, scales, xh, c, stream)
+                         : dispatch_L<4, false>(L, x, M, codes, scales, xh, c, stream);
+    if (bits == 8)
+        hipLaunchKernelGGL(quantize_rows_generic_kernel<8>, dim3(M), dim3(256), 0, stream, x, K, codes,
+                           scales, xh);
+    else
+        hipLaunchKernelGGL(quantize_rows_generic_kernel<4>, dim3(M), dim3(256), 0, stream, x, K, codes,
+                           scales, xh);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,149 @@
+"""Host-side checks of libbitnet_hip.so: exported symbols, the offline packer against the oracle,
+and argument validation (every failing check returns before anything reaches the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+import ternary_weight_bit_bitlinear_amd as tb
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "hbitlinear_forward" in names and "bitnet_pack_weights" in names
+    L = ctypes.CDLL(tb.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", tb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_library_is_independent_of_the_oracle():
+    out = subprocess.run(["nm", "-D", tb.LIB_PATH], capture_output=True, text=True).stdout
+    assert "bitnet_ref_" not in out
+    ldd = subprocess.run(["ldd", tb.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in ldd
+    csrc = os.path.join(ROOT, "ternary_weight_bit_bitlinear_amd", "csrc")
+    for f in os.listdir(csrc):
+        assert "oracle" not in open(os.path.join(csrc, f)).read().lower(), f
+
+
+def test_abi_version_and_status_strings():
+    assert tb.bitnet_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert tb.bitnet_status_string(s) != "unknown status"
+    assert tb.bitnet_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 5), (4, 64), (7, 319), (5, 320), (9, 321),
+                                 (16, 1000), (256, 256), (64, 4096), (33, 16384)])
+def test_packer_matches_oracle_bytes(N, K):
+    W = si.gaussian_weights(9, N, K)
+    packed, g = tb.bitnet_pack_weights(W)
+    opacked, og, ot = oracle.pack_weights(W)
+    assert np.float32(g) == og
+    assert packed.size == oracle.packed_bytes(N, K) == tb.bitnet_packed_bytes(N, K)
+    assert np.array_equal(packed, opacked)
+    assert np.array_equal(tb.bitnet_unpack_weights(packed, N, K), ot)
+
+
+def test_packer_matches_oracle_at_full_size():
+    W = si.gaussian_weights(3, 4096, 4096)
+    packed, g = tb.bitnet_pack_weights(W)
+    opacked, og, _ = oracle.pack_weights(W)
+    assert np.float32(g) == og and np.array_equal(packed, opacked)
+
+
+def test_packer_zero_and_worked_example():
+    packed, g = tb.bitnet_pack_weights(np.zeros((2, 10), np.float32))
+    assert g == 0.0 and np.all(packed == 121)
+    # a row whose weights at k = 0, 64, 128, 192, 256 ternarise to (1, -1, 0, 1, 0)
+    W = np.zeros((1, 320), np.float32)
+    W[0, :] = 0.0
+    W[0, [0, 64, 128, 192, 256]] = [1.0, -1.0, 0.0, 1.0, 0.0]
+    W[0, 1] = 1.0          # keeps gamma small enough that +-1 stay +-1
+    packed, g = tb.bitnet_pack_weights(W)
+    assert packed[0] == 178
+
+
+def test_unpack_rejects_bad_bytes():
+    packed, _ = tb.bitnet_pack_weights(np.ones((1, 10), np.float32))
+    bad = packed.copy(); bad[0] = 243
+    with pytest.raises(tb.BitnetError) as e:
+        tb.bitnet_unpack_weights(bad, 1, 10)
+    assert e.value.status == tb.BITNET_ERR_FORMAT
+    bad = packed.copy(); bad[40] = 0       # a padding trit of -1
+    with pytest.raises(tb.BitnetError):
+        tb.bitnet_unpack_weights(bad, 1, 10)
+
+
+def _size(fn, *args):
+    out = ctypes.c_size_t(0)
+    return fn(*args, ctypes.byref(out)), out.value
+
+
+def test_size_queries():
+    L = tb.lib()
+    assert _size(L.hbitlinear_codes_bytes, 16, 4096, 8) == (0, 16 * 4096)
+    assert _size(L.hbitlinear_codes_bytes, 16, 4096, 4) == (0, 8 * 4096)
+    rc, ws = _size(L.hbitlinear_workspace_bytes, 16, 4096, 8)
+    assert rc == 0 and ws == 65536 + 256
+    assert _size(L.bitnet_packed_bytes, 4096, 4096) == (0, 4096 * 832)
+    assert L.hbitlinear_workspace_bytes(16, 4096, 8, None) == tb.BITNET_ERR_NULL
+    assert _size(L.hbitlinear_workspace_bytes, 0, 4096, 8)[0] == tb.BITNET_ERR_SHAPE
+    assert _size(L.hbitlinear_workspace_bytes, 4, 4096, 5)[0] == tb.BITNET_ERR_UNSUPPORTED
+    assert _size(L.bitnet_packed_bytes, -1, 5)[0] == tb.BITNET_ERR_SHAPE
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+NUL = ctypes.c_void_p(None)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (x, M, K, N, bits, had, out, packed, ws, ws_bytes)
+    ((NUL, 4, 4096, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_NULL),
+    ((FAKE, 4, 4096, 64, 8, 0, NUL, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_NULL),
+    ((FAKE, 4, 4096, 64, 8, 0, FAKE, NUL, FAKE, 1 << 20), tb.BITNET_ERR_NULL),
+    ((FAKE, 0, 4096, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_SHAPE),
+    ((FAKE, 4, 0, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_SHAPE),
+    ((FAKE, 4, 4096, -1, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_SHAPE),
+    ((FAKE, 4, 4096, 64, 2, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 4096, 64, 8, 2, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 4000, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 4032, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 128, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 32768, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 30), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 4, 4096, 64, 8, 0, FAKE, FAKE, NUL, 1 << 20), tb.BITNET_ERR_WORKSPACE),
+    ((FAKE, 4, 4096, 64, 8, 0, FAKE, FAKE, FAKE, 4 * 4096), tb.BITNET_ERR_WORKSPACE),
+])
+def test_forward_validation(args, expect):
+    x, M, K, N, bits, had, out, packed, ws, wsb = args
+    rc = tb.lib().hbitlinear_forward(x, M, K, N, bits, had, out, packed, ctypes.c_float(1.0), ws,
+                                     wsb, NUL)
+    assert rc == expect
+
+
+def test_stage_validation():
+    L = tb.lib()
+    assert L.hbitlinear_quantize(NUL, 4, 256, 8, 1, FAKE, FAKE, NUL, NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_quantize(FAKE, 4, 200, 8, 1, FAKE, FAKE, NUL, NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_ternary_gemm_i32(FAKE, 4, 256, 8, 8, NUL, FAKE, NUL) == tb.BITNET_ERR_NULL
+    assert L.bitnet_ternary_gemm_i32(FAKE, 4, 256, 0, 8, FAKE, FAKE, NUL) == tb.BITNET_ERR_SHAPE
+    assert L.hbitlinear_gemm_dequant(FAKE, NUL, 4, 256, 8, 4, FAKE, ctypes.c_float(1.0), FAKE,
+                                     NUL) == tb.BITNET_ERR_NULL
+    assert L.bitnet_pack_weights(NUL, 1, 1, FAKE, FAKE) == tb.BITNET_ERR_NULL

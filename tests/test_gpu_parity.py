@@ -1,0 +1,271 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
+
+Tolerances:
+  - post-Hadamard fp32 values: max |gpu - oracle| / row absmax <= 1e-5 (the kernel runs the
+    oracle's butterfly order, so they are expected to be identical);
+  - codes: at most 1e-4 of them differ, each by exactly 1;
+  - int32 products: bit-exact when both sides get the same codes;
+  - outputs: rows whose codes match are bit-exact, all rows within 1e-3 relative (elementwise,
+    against max(|y_ref|, 1e-3 * row max)); rows with a code difference are checked exactly
+    against the oracle's product and epilogue run on the GPU's own codes.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def tb():
+    import ternary_weight_bit_bitlinear_amd as m
+    m.lib()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def codes_to_int8(codes_u8, M, K, bits):
+    c = codes_u8.cpu().numpy()
+    if bits == 8:
+        return c.view(np.int8).reshape(M, K)
+    return oracle.unpack_int4(c.reshape(M, K // 2), K)
+
+
+def check_quant(tb, x, bits, had, rows=None, label=""):
+    """Run the GPU activation stage on x (all rows); compare the sampled rows with the oracle.
+    Returns the GPU codes (int8, sampled rows) and whether they equal the oracle's."""
+    M, K = x.shape
+    xd = dev(x)
+    codes, scales, xh = tb.hbitlinear_quantize(xd, bits, had, want_xh=True)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    oq, os_, oxh = oracle.quantize(x[rows], bits, had, want_xh=True)
+    gxh = xh.cpu().numpy()[rows]
+    gs = scales.cpu().numpy()[rows]
+    gq = codes_to_int8(codes, M, K, bits)[rows]
+    amax = np.maximum(np.max(np.abs(oxh), axis=1, keepdims=True), 1e-30)
+    rel = float(np.max(np.abs(gxh - oxh) / amax))
+    assert rel <= 1e-5, f"{label} post-Hadamard rel diff {rel}"
+    diff = gq.astype(np.int32) - oq.astype(np.int32)
+    nd = int(np.count_nonzero(diff))
+    assert nd <= 1e-4 * diff.size, f"{label} {nd} codes differ"
+    assert np.all(np.abs(diff) <= 1)
+    same_codes = nd == 0
+    if same_codes:
+        np.testing.assert_array_equal(gs, os_)
+    else:
+        assert np.allclose(gs, os_, rtol=1e-5, atol=0)
+    say(f"  {label}: xh rel {rel:.2e}, codes differing {nd}/{diff.size}")
+    return gq, gs, same_codes
+
+
+# ---------------------------------------------------------------- activation stage ----
+
+@pytest.mark.parametrize("K", [256, 512, 1024, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("had", [True, False])
+def test_quantize_all_widths(tb, K, bits, had):
+    M = 7
+    x = si.normal(si.seed_for(1, 7) + K, M * K).reshape(M, K)
+    x[2] = 0.0                       # zero row: codes 0, scale 0
+    x[3] = 0.0; x[3, K // 3] = 5.0   # single spike
+    x[4, 5] *= 40.0                  # outlier channel
+    check_quant(tb, x, bits, had, label=f"K={K} bits={bits} had={had}")
+
+
+@pytest.mark.parametrize("K", [64, 320, 960, 4032])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_generic_widths(tb, K, bits):
+    x = si.normal(si.seed_for(1, 8) + K, 9 * K).reshape(9, K)
+    x[1] = 0.0
+    check_quant(tb, x, bits, False, label=f"generic K={K} bits={bits}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_rounding_ties(tb, bits):
+    # integer-grid rows with max Qp: inv = 1, so x + 0.5 values sit exactly on ties
+    qp = 2 ** (bits - 1) - 1
+    K = 512
+    rng = np.random.default_rng(bits)
+    x = rng.integers(-qp, qp, size=(6, K)).astype(np.float32) + np.float32(0.5)
+    x[:, 0] = qp
+    gq, gs, same = check_quant(tb, x, bits, False, label="ties")
+    assert same
+    assert np.all(gs == 1.0)
+
+
+# ------------------------------------------------------------------ ternary product ----
+
+GEMM_SHAPES = [(16, 256, 256), (1, 64, 64), (300, 200, 1024), (257, 513, 4096), (64, 64, 320),
+               (33, 17, 960), (512, 256, 16384), (5, 1000, 4032)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gemm_i32_bit_exact(tb, M, N, K, bits):
+    say(f"  gemm M={M} N={N} K={K} bits={bits}")
+    qp = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(M * 7 + N * 3 + K + bits)
+    q = rng.integers(-qp - 1, qp + 1, size=(M, K)).astype(np.int8)
+    W = si.gaussian_weights(2, N, K, layer=M % 5)
+    packed, g = tb.bitnet_pack_weights(W)
+    t = oracle.unpack(packed, N, K)
+    cb = q.view(np.uint8) if bits == 8 else oracle.pack_int4(q)
+    acc = tb.bitnet_ternary_gemm_i32(dev(cb.reshape(-1)), M, K, N, bits, dev(packed))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.gemm(q, t))
+
+
+def test_gemm_extreme_sums(tb):
+    # |acc| reaches 128 * 16384 = 2^21: every code -128, every weight +1 or -1
+    M, N, K = 3, 64, 16384
+    q = np.full((M, K), -128, np.int8)
+    W = np.ones((N, K), np.float32)
+    W[1::2] = -1.0
+    packed, _ = tb.bitnet_pack_weights(W)
+    acc = tb.bitnet_ternary_gemm_i32(dev(q.view(np.uint8).reshape(-1)), M, K, N, 8, dev(packed))
+    torch.cuda.synchronize()
+    a = acc.cpu().numpy()
+    assert np.all(a[:, 0::2] == -128 * K) and np.all(a[:, 1::2] == 128 * K)
+
+
+# ------------------------------------------------------------------------ forward ----
+
+_cache = {}
+
+
+def linear_inputs(config, idx=0, M=None):
+    key = (config, idx, M)
+    if key not in _cache:
+        wl = si.workload(config, M)
+        lin = wl.linears[idx]
+        x = si.activations(config, lin)
+        W = si.weights(config, lin)
+        _cache.clear()
+        _cache[key] = (lin, x, W)
+    return _cache[key]
+
+
+def check_forward(tb, lin, x, W, rows, label):
+    M, K, N = lin.M, lin.K, lin.N
+    packed, g = tb.bitnet_pack_weights(W)
+    opacked, og, t = oracle.pack_weights(W)
+    assert np.array_equal(packed, opacked) and np.float32(g) == og
+    xd = dev(x)
+    pd = dev(packed)
+    y = tb.hbitlinear_forward(xd, N, lin.act_bits, lin.use_hadamard, pd, g)
+    # the stage exports on the same input, for the codes the forward used
+    codes, scales = tb.hbitlinear_quantize(xd, lin.act_bits, lin.use_hadamard)
+    torch.cuda.synchronize()
+    rows = np.asarray(rows)
+    gy = y.cpu().numpy()[rows]
+    gq = codes_to_int8(codes, M, K, lin.act_bits)[rows]
+    gs = scales.cpu().numpy()[rows]
+    del y, codes, scales, xd
+    xs = x[rows]
+    oy = oracle.forward(xs, opacked, og, N, lin.act_bits, lin.use_hadamard)
+    oq, os_ = oracle.quantize(xs, lin.act_bits, lin.use_hadamard)
+    match = np.all(gq == oq, axis=1)
+    # rows with identical codes: bit-exact
+    np.testing.assert_array_equal(gy[match], oy[match])
+    # every row: 1e-3 relative
+    scale = np.maximum(np.abs(oy), 1e-3 * np.max(np.abs(oy), axis=1, keepdims=True))
+    assert np.all(np.abs(gy - oy) <= 1e-3 * scale + 0.0), f"{label}: relative error above 1e-3"
+    # rows with a code difference: exact against the oracle fed the GPU's codes
+    if not np.all(match):
+        y2 = oracle.epilogue(oracle.gemm(gq[~match], t), gs[~match], og)
+        np.testing.assert_array_equal(gy[~match], y2)
+    say(f"  {label}: {int(np.sum(match))}/{len(rows)} sampled rows with identical codes")
+
+
+def sample_rows(M, n, seed):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    r = np.sort(rng.choice(M, size=n - 2, replace=False))
+    return np.unique(np.concatenate([[0], r, [M - 1]]))
+
+
+def test_forward_config1_tiny(tb):
+    lin, x, W = linear_inputs(1)
+    check_forward(tb, lin, x, W, np.arange(lin.M), "cfg1 tiny")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_forward_config2_decode(tb, M):
+    lin, x, W = linear_inputs(2, 0, M)
+    check_forward(tb, lin, x, W, np.arange(M), f"cfg2 decode M={M}")
+
+
+def test_forward_config3_wo(tb):
+    lin, x, W = linear_inputs(3)
+    check_quant(tb, x, 4, True, rows=sample_rows(lin.M, 512, 3), label="cfg3 quant")
+    check_forward(tb, lin, x, W, sample_rows(lin.M, 48, 3), "cfg3 Wo")
+
+
+def test_forward_config4_wdown(tb):
+    lin, x, W = linear_inputs(4)
+    check_quant(tb, x, 4, True, rows=sample_rows(lin.M, 256, 4), label="cfg4 quant")
+    check_forward(tb, lin, x, W, sample_rows(lin.M, 24, 4), "cfg4 Wdown")
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_forward_config5_block(tb, idx):
+    lin, x, W = linear_inputs(5, idx)
+    check_forward(tb, lin, x, W, sample_rows(lin.M, 16, 50 + idx), f"cfg5 {lin.name}")
+
+
+@pytest.mark.parametrize("M,N,K,bits,had", [(300, 200, 4096, 4, True), (1, 17, 256, 8, True),
+                                            (257, 1000, 8192, 8, True), (5, 64, 64, 8, False),
+                                            (70, 300, 960, 4, False), (2, 4096, 16384, 4, True)])
+def test_forward_ragged_shapes(tb, M, N, K, bits, had):
+    x = si.laplace(si.seed_for(6, 0) + M + K, M * K, 0.05).reshape(M, K)
+    x[M // 2] = 0.0
+    W = si.gaussian_weights(6, N, K)
+    lin = si.Linear("ragged", M, K, N, bits, had, "x")
+    check_forward(tb, lin, x, W, np.arange(M), f"ragged M={M} N={N} K={K} b={bits} h={had}")
+
+
+def test_forward_zero_input_gives_zero(tb):
+    M, N, K = 4, 64, 4096
+    W = si.gaussian_weights(7, N, K)
+    packed, g = tb.bitnet_pack_weights(W)
+    y = tb.hbitlinear_forward(dev(np.zeros((M, K), np.float32)), N, 4, True, dev(packed), g)
+    torch.cuda.synchronize()
+    assert not np.any(y.cpu().numpy())
+
+
+def test_forward_is_deterministic_and_stream_safe(tb):
+    lin, x, W = linear_inputs(3, 0, 512)
+    packed, g = tb.bitnet_pack_weights(W)
+    xd, pd = dev(x), dev(packed)
+    y1 = tb.hbitlinear_forward(xd, lin.N, 4, True, pd, g)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y2 = tb.hbitlinear_forward(xd, lin.N, 4, True, pd, g, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_forward_rejects_small_workspace(tb):
+    M, N, K = 4, 64, 256
+    packed, g = tb.bitnet_pack_weights(si.gaussian_weights(7, N, K))
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tb.BitnetError) as e:
+        tb.hbitlinear_forward(dev(np.ones((M, K), np.float32)), N, 8, True, dev(packed), g,
+                              workspace=ws)
+    assert e.value.status == tb.BITNET_ERR_WORKSPACE
