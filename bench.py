@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the H-BitLinear forward on one MI355X.
+
+Headline workload: plain BitLinear W1.58A8 at decode shape (M = 16 tokens, K = N = 4096, INT8
+activations, no Hadamard), streamed through L = 128 distinct weight matrices (430 MB, more than
+the 256 MB Infinity Cache), one layer after another on one stream.  One step = every layer's
+activation stage + ternary GEMM with fused dequantisation (the same two kernels
+hbitlinear_forward runs).  tokens/s counts a token once per layer forward:
+value = M * L * steps / time.
+
+Also reported (same JSON line): decode at M = 1 and 4, and the large-M H-BitLinear workloads
+(Wo M=4096 K=N=4096; Wdown M=8192 K=16384 N=4096; all seven linears of a 7B block at
+M=16384), each with its int8 MFMA roofline fraction.
+
+Inputs are seeded synthetic data (seeded_inputs) resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
+METRIC = "H-BitLinear tokens/s + effective int-TOPS, % of HBM/int8-MFMA roofline"
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=128)
+    p.add_argument("--M", type=int, default=16)
+    p.add_argument("--large-steps", type=int, default=10)
+    p.add_argument("--no-large", action="store_true", help="skip the large-M workloads")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", choices=["decode", "wo", "wdown", "block"], default=None,
+                   help="run one workload only (profiling)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events around every launch of one kernel, recorded on the launching stream."""
+
+    def __init__(self, torch, n):
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+        self.i = 0
+
+    def begin(self, stream):
+        self.pairs[self.i][0].record(stream)
+
+    def end(self, stream):
+        self.pairs[self.i][1].record(stream)
+        self.i += 1
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
+
+
+def canonical_packed_bytes(N, K):
+    # five trits per byte with nothing wasted: the algorithmic weight bytes
+    return N * ((K + 4) // 5)
+
+
+# --------------------------------------------------------------------------- decode ----
+
+def make_decode(torch, tb, si, M, L, unique=4):
+    """L distinct packed 4096x4096 weight buffers (copies of `unique` seeded matrices at
+    distinct addresses) and L distinct seeded inputs."""
+    K = N = 4096
+    dev = torch.device("cuda:0")
+    packs = []
+    for u in range(unique):
+        W = si.gaussian_weights(2, N, K, layer=u)
+        packed, g = tb.bitnet_pack_weights(W)
+        packs.append((torch.from_numpy(packed).to(dev), g))
+    ws, gs = [], []
+    for l in range(L):
+        p, g = packs[l % unique]
+        ws.append(p.clone())
+        gs.append(g)
+    x = torch.from_numpy(si.normal(si.seed_for(2, 0), L * M * K).reshape(L, M, K)).to(dev)
+    return dict(M=M, K=K, N=N, L=L, x=x, w=ws, g=gs, packs=packs)
+
+
+def run_decode(torch, tb, d, steps, warmup):
+    M, K, N, L = d["M"], d["K"], d["N"], d["L"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    codes = torch.empty(tb.hbitlinear_codes_bytes(M, K, 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+
+    def step(tq=None, tg=None):
+        for l in range(L):
+            if tq: tq.begin(stream)
+            tb.hbitlinear_quantize(d["x"][l], 8, False, codes=codes, scales=scales, stream=stream)
+            if tq: tq.end(stream)
+            if tg: tg.begin(stream)
+            tb.hbitlinear_gemm_dequant(codes, scales, M, K, N, 8, d["w"][l], d["g"][l], out=y[l],
+                                       stream=stream)
+            if tg: tg.end(stream)
+
+    for _ in range(warmup):
+        step()
+    tq, tg = Timer(torch, steps * L), Timer(torch, steps * L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(tq, tg)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gemm_ms = tg.mean_ms()
+    quant_ms = tq.mean_ms()
+    bytes_gemm = canonical_packed_bytes(N, K) + M * K + 4 * M + 4 * M * N
+    ops = 2.0 * M * N * K
+    return dict(
+        seconds=dt, ms_per_step=1e3 * dt / steps,
+        tokens_per_s=M * L * steps / dt,
+        int_tops=ops * L * steps / dt / 1e12,
+        gemm_us=1e3 * gemm_ms, quant_us=1e3 * quant_ms,
+        gemm_bytes=bytes_gemm,
+        gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9,
+    )
+
+
+def cpu_baseline_decode(si, oracle, d, tb, layers=2):
+    """The oracle forward on `layers` of the decode layers (host only)."""
+    M, K, N = d["M"], d["K"], d["N"]
+    xs = d["x"][:layers].cpu().numpy()
+    packs = [(d["packs"][l % len(d["packs"])][0].cpu().numpy(), d["g"][l]) for l in range(layers)]
+    t0 = time.perf_counter()
+    for l in range(layers):
+        oracle.forward(xs[l], packs[l][0], packs[l][1], N, 8, False)
+    dt = time.perf_counter() - t0
+    return dict(value=M * layers / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{layers} of the {d['L']} layers at M={M} (unpack + quantise + add/sub "
+                       f"product + epilogue per layer), {dt:.1f} s")
+
+
+# -------------------------------------------------------------------------- large M ----
+
+def run_large(torch, tb, si, config, steps, warmup):
+    wl = si.workload(config)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    lins = []
+    xcache = {}
+    for lin in wl.linears:
+        key = lin.x_kind
+        if key not in xcache:
+            xcache[key] = torch.from_numpy(si.activations(config, lin)).to(dev)
+        W = si.weights(config, lin)
+        packed, g = tb.bitnet_pack_weights(W)
+        del W
+        codes = torch.empty(tb.hbitlinear_codes_bytes(lin.M, lin.K, lin.act_bits), dtype=torch.uint8,
+                            device=dev)
+        scales = torch.empty(lin.M, dtype=torch.float32, device=dev)
+        out = torch.empty((lin.M, lin.N), dtype=torch.float32, device=dev)
+        lins.append((lin, xcache[key], torch.from_numpy(packed).to(dev), g, codes, scales, out))
+    n = len(lins)
+
+    def step(tq=None, tg=None):
+        for j, (lin, x, pw, g, codes, scales, out) in enumerate(lins):
+            if tq: tq[j].begin(stream)
+            tb.hbitlinear_quantize(x, lin.act_bits, lin.use_hadamard, codes=codes, scales=scales,
+                                   stream=stream)
+            if tq: tq[j].end(stream)
+            if tg: tg[j].begin(stream)
+            tb.hbitlinear_gemm_dequant(codes, scales, lin.M, lin.K, lin.N, lin.act_bits, pw, g,
+                                       out=out, stream=stream)
+            if tg: tg[j].end(stream)
+
+    for _ in range(warmup):
+        step()
+    tq = [Timer(torch, steps) for _ in range(n)]
+    tg = [Timer(torch, steps) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(tq, tg)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    M = wl.linears[0].M
+    ops = sum(2.0 * l.M * l.N * l.K for l in wl.linears)
+    gemm_s = sum(t.mean_ms() for t in tg) * 1e-3
+    quant_s = sum(t.mean_ms() for t in tq) * 1e-3
+    per = {}
+    for j, (lin, *_rest) in enumerate(lins):
+        g_ms = tg[j].mean_ms()
+        q_ms = tq[j].mean_ms()
+        qbytes = 4 * lin.M * lin.K + lin.M * lin.K * lin.act_bits // 8 + 4 * lin.M
+        per[lin.name] = dict(gemm_us=1e3 * g_ms, quant_us=1e3 * q_ms,
+                             gemm_tops=2.0 * lin.M * lin.N * lin.K / (g_ms * 1e-3) / 1e12,
+                             quant_gbs=qbytes / (q_ms * 1e-3) / 1e9)
+    res = dict(workload=wl.name, M=M, ms_per_step=1e3 * dt / steps,
+               tokens_per_s=M * steps / dt, int_tops=ops * steps / dt / 1e12,
+               gemm_int_tops=ops / gemm_s / 1e12,
+               gemm_mfma_frac=ops / gemm_s / 1e12 / INT8_PEAK_TOPS,
+               end_to_end_mfma_frac=ops * steps / dt / 1e12 / INT8_PEAK_TOPS,
+               quant_share=quant_s / (quant_s + gemm_s), linears=per)
+    del lins, xcache
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", flush=True)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import seeded_inputs as si
+    import ternary_weight_bit_bitlinear_amd as tb
+    tb.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    result = {}
+    if args.only in (None, "decode"):
+        log(f"[bench] decode: preparing M={args.M}, {args.layers} layers")
+        d = make_decode(torch, tb, si, args.M, args.layers)
+        log("[bench] decode: timing")
+        r = run_decode(torch, tb, d, args.steps, args.warmup)
+        log(f"[bench] decode: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.2f} us "
+            f"({r['gemm_gbs']:.0f} GB/s), quant {r['quant_us']:.2f} us")
+        others = {}
+        for m in (1, 4):
+            dm = make_decode(torch, tb, si, m, args.layers)
+            rm = run_decode(torch, tb, dm, max(2, args.steps // 4), 1)
+            others[f"M{m}"] = dict(tokens_per_s=rm["tokens_per_s"], gemm_us=rm["gemm_us"],
+                                   gemm_gbs=rm["gemm_gbs"], hbm_frac=rm["gemm_gbs"] / HBM_PEAK_GBS)
+            log(f"[bench] decode M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm {rm['gemm_us']:.2f} us")
+            del dm
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+            log("[bench] cpu baseline (oracle)")
+            cpu = cpu_baseline_decode(si, oracle, d, tb)
+        result = {
+            "metric": METRIC,
+            "value": r["tokens_per_s"],
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": r["ms_per_step"],
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "int8",
+            "data": "synthetic",
+            "config": {"workload": f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_L{d['L']}",
+                       "M": d["M"], "K": 4096, "N": 4096, "layers": d["L"], "act_bits": 8,
+                       "use_hadamard": False,
+                       "tokens_per_s": "M * layers * steps / seconds (a token counts once per layer)"},
+            "int_tops": r["int_tops"],
+            "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gemm_tern_kernel<8,true>", "launch_us": r["gemm_us"],
+                         "algorithmic_bytes_per_launch": r["gemm_bytes"]},
+            "quant_kernel_us": r["quant_us"],
+            "decode_other_M": others,
+            "cpu_baseline": cpu,
+        }
+        del d
+        torch.cuda.empty_cache()
+
+    if not args.no_large and args.only in (None, "wo", "wdown", "block"):
+        large = {}
+        for name, cfg in (("wo", 3), ("wdown", 4), ("block", 5)):
+            if args.only not in (None, name):
+                continue
+            log(f"[bench] {name}: preparing")
+            r = run_large(torch, tb, si, cfg, args.large_steps, 2)
+            log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
+                f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
+            large[name] = r
+        if result:
+            result["large_m"] = large
+        else:
+            name, r = next(iter(large.items()))
+            result = {"metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                      "steps": args.large_steps, "warmup": 2, "ms_per_step": r["ms_per_step"],
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "int8", "data": "synthetic", "config": {"workload": r["workload"]},
+                      "large_m": large}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
