@@ -2,11 +2,12 @@
 """Benchmark of the H-BitLinear forward on one MI355X.
 
 Headline workload: plain BitLinear W1.58A8 at decode shape (M = 16 tokens, K = N = 4096, INT8
-activations, no Hadamard), streamed through L = 128 distinct weight matrices (430 MB, more than
-the 256 MB Infinity Cache), one layer after another on one stream.  One step = every layer's
-activation stage + ternary GEMM with fused dequantisation (the same two kernels
-hbitlinear_forward runs).  tokens/s counts a token once per layer forward:
-value = M * L * steps / time.
+activations, no Hadamard) over L = 128 distinct weight matrices (430 MB, more than the 256 MB
+Infinity Cache, so the weights stream from HBM).  One step = the activation stage over the
+L*M token rows and one grouped product launch over the L layers -- exactly the two kernels
+hbitlinear_forward_grouped runs.  tokens/s counts a token once per layer forward:
+value = M * L * steps / time.  The same layers run one call after another are reported too
+("decode_sequential").
 
 Also reported (same JSON line): decode at M = 1 and 4, and the large-M H-BitLinear workloads
 (Wo M=4096 K=N=4096; Wdown M=8192 K=16384 N=4096; all seven linears of a 7B block at
@@ -92,10 +93,54 @@ def make_decode(torch, tb, si, M, L, unique=4):
         ws.append(p.clone())
         gs.append(g)
     x = torch.from_numpy(si.normal(si.seed_for(2, 0), L * M * K).reshape(L, M, K)).to(dev)
-    return dict(M=M, K=K, N=N, L=L, x=x, w=ws, g=gs, packs=packs)
+    ptrs = torch.tensor([w.data_ptr() for w in ws], dtype=torch.int64, device=dev)
+    wsc = torch.tensor(gs, dtype=torch.float32, device=dev)
+    return dict(M=M, K=K, N=N, L=L, x=x, w=ws, g=gs, packs=packs, ptrs=ptrs, wsc=wsc)
+
+
+def decode_gemm_bytes(M, K, N):
+    return canonical_packed_bytes(N, K) + M * K + 4 * M + 4 * M * N
+
+
+def run_decode_grouped(torch, tb, d, steps, warmup):
+    """One step = the activation stage over all L*M rows, then one grouped product launch
+    over the L layers (what hbitlinear_forward_grouped runs)."""
+    M, K, N, L = d["M"], d["K"], d["N"], d["L"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    codes = torch.empty(tb.hbitlinear_codes_bytes(L * M, K, 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty(L * M, dtype=torch.float32, device=dev)
+    y = torch.empty((L, M, N), dtype=torch.float32, device=dev)
+    xf = d["x"].view(L * M, K)
+
+    def step(tq=None, tg=None):
+        if tq: tq.begin(stream)
+        tb.hbitlinear_quantize(xf, 8, False, codes=codes, scales=scales, stream=stream)
+        if tq: tq.end(stream)
+        if tg: tg.begin(stream)
+        tb.hbitlinear_gemm_dequant_grouped(codes, scales, L, M, K, N, 8, d["ptrs"], d["wsc"], out=y,
+                                           stream=stream)
+        if tg: tg.end(stream)
+
+    for _ in range(warmup):
+        step()
+    tq, tg = Timer(torch, steps), Timer(torch, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(tq, tg)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gemm_ms = tg.mean_ms()
+    bytes_gemm = L * decode_gemm_bytes(M, K, N)
+    return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=M * L * steps / dt,
+                int_tops=2.0 * M * N * K * L * steps / dt / 1e12, gemm_us=1e3 * gemm_ms,
+                quant_us=1e3 * tq.mean_ms(), gemm_bytes=bytes_gemm,
+                gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9)
 
 
 def run_decode(torch, tb, d, steps, warmup):
+    """Layer after layer: one activation stage and one product launch per layer."""
     M, K, N, L = d["M"], d["K"], d["N"], d["L"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -123,17 +168,11 @@ def run_decode(torch, tb, d, steps, warmup):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     gemm_ms = tg.mean_ms()
-    quant_ms = tq.mean_ms()
-    bytes_gemm = canonical_packed_bytes(N, K) + M * K + 4 * M + 4 * M * N
-    ops = 2.0 * M * N * K
-    return dict(
-        seconds=dt, ms_per_step=1e3 * dt / steps,
-        tokens_per_s=M * L * steps / dt,
-        int_tops=ops * L * steps / dt / 1e12,
-        gemm_us=1e3 * gemm_ms, quant_us=1e3 * quant_ms,
-        gemm_bytes=bytes_gemm,
-        gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9,
-    )
+    bytes_gemm = decode_gemm_bytes(M, K, N)
+    return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=M * L * steps / dt,
+                int_tops=2.0 * M * N * K * L * steps / dt / 1e12, gemm_us=1e3 * gemm_ms,
+                quant_us=1e3 * tq.mean_ms(), gemm_bytes=bytes_gemm,
+                gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9)
 
 
 def cpu_baseline_decode(si, oracle, d, tb, layers=2):
@@ -237,17 +276,24 @@ def main():
     if args.only in (None, "decode"):
         log(f"[bench] decode: preparing M={args.M}, {args.layers} layers")
         d = make_decode(torch, tb, si, args.M, args.layers)
-        log("[bench] decode: timing")
-        r = run_decode(torch, tb, d, args.steps, args.warmup)
-        log(f"[bench] decode: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.2f} us "
-            f"({r['gemm_gbs']:.0f} GB/s), quant {r['quant_us']:.2f} us")
+        log("[bench] decode: timing (grouped)")
+        r = run_decode_grouped(torch, tb, d, args.steps, args.warmup)
+        log(f"[bench] decode grouped: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.1f} us "
+            f"({r['gemm_gbs']:.0f} GB/s), quant {r['quant_us']:.1f} us")
+        rs = run_decode(torch, tb, d, max(2, args.steps // 4), 1)
+        log(f"[bench] decode sequential: {rs['tokens_per_s']:.4g} tokens/s, gemm {rs['gemm_us']:.2f} us "
+            f"per layer ({rs['gemm_gbs']:.0f} GB/s)")
+        sequential = dict(tokens_per_s=rs["tokens_per_s"], gemm_us_per_layer=rs["gemm_us"],
+                          quant_us_per_layer=rs["quant_us"], gemm_gbs=rs["gemm_gbs"],
+                          hbm_frac=rs["gemm_gbs"] / HBM_PEAK_GBS)
         others = {}
         for m in (1, 4):
             dm = make_decode(torch, tb, si, m, args.layers)
-            rm = run_decode(torch, tb, dm, max(2, args.steps // 4), 1)
+            rm = run_decode_grouped(torch, tb, dm, max(2, args.steps // 2), 1)
             others[f"M{m}"] = dict(tokens_per_s=rm["tokens_per_s"], gemm_us=rm["gemm_us"],
                                    gemm_gbs=rm["gemm_gbs"], hbm_frac=rm["gemm_gbs"] / HBM_PEAK_GBS)
-            log(f"[bench] decode M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm {rm['gemm_us']:.2f} us")
+            log(f"[bench] decode grouped M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm "
+                f"{rm['gemm_us']:.1f} us ({rm['gemm_gbs']:.0f} GB/s)")
             del dm
         cpu = None
         if not args.no_cpu_baseline:
@@ -267,16 +313,19 @@ def main():
             "vs_baseline": None,
             "dtype": "int8",
             "data": "synthetic",
-            "config": {"workload": f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_L{d['L']}",
+            "config": {"workload": f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_grouped_L{d['L']}",
                        "M": d["M"], "K": 4096, "N": 4096, "layers": d["L"], "act_bits": 8,
                        "use_hadamard": False,
+                       "step": "activation stage over L*M rows + one grouped product launch over "
+                               "L distinct weight matrices (hbitlinear_forward_grouped)",
                        "tokens_per_s": "M * layers * steps / seconds (a token counts once per layer)"},
             "int_tops": r["int_tops"],
             "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "gemm_tern_kernel<8,true>", "launch_us": r["gemm_us"],
+                         "kernel": "gemm_decode_kernel<8,true>", "launch_us": r["gemm_us"],
                          "algorithmic_bytes_per_launch": r["gemm_bytes"]},
             "quant_kernel_us": r["quant_us"],
+            "decode_sequential": sequential,
             "decode_other_M": others,
             "cpu_baseline": cpu,
         }

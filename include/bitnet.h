@@ -59,13 +59,19 @@ int bitnet_abi_version(void);
 /* Offline weight preparation (host memory, synchronous).                                */
 /* ------------------------------------------------------------------------------------ */
 
-/* Size in bytes of a packed N x K weight: N * 64 * ceil(K / 320).
- * Packed layout: row n is 64 * ceil(K/320) bytes; byte b of 320-weight block B of that row
- * holds the weights k = 320 B + b + 64 i (i = 0..4) as base-3 digit i, digit = t + 1, digit 0
- * the most significant: byte = 81 d0 + 27 d1 + 9 d2 + 3 d3 + d4 (so the digits 2,0,1,2,1 give
- * 178, the 2B4T write-up's section 1.1 example).  Positions k >= K hold t = 0.
- * Which five weights share a byte is this library's choice (the pages fix only the byte
- * code): grouping weights 64 apart lets one 16-byte load decode to five 64-wide MFMA slices. */
+/* Size in bytes of a packed N x K weight: 16 * ceil(N / 16) * 64 * ceil(K / 320).
+ * Byte code: five trits per byte, base 3, digit = t + 1, the first digit most significant,
+ * byte = 81 d0 + 27 d1 + 9 d2 + 3 d3 + d4 (so the digits 2,0,1,2,1 give 178, the 2B4T
+ * write-up's section 1.1 example).
+ * Layout (this library's choice; the pages fix only the byte code):
+ *   - which weights share a byte: row n is cut into blocks of 320 weights, 64 bytes each;
+ *     byte b of block B holds the weights k = 320 B + b + 64 i as digit i (i = 0..4);
+ *   - where a byte sits: rows go in groups of 16 (the last group padded with zero rows);
+ *     group G and block B form one 1024-byte tile at offset (G * ceil(K/320) + B) * 1024, and
+ *     byte b of row n sits in it at ((b / 16) * 16 + n % 16) * 16 + b % 16.
+ * Weights at k >= K and pad rows n >= N are t = 0.  Grouping weights 64 apart lets one
+ * 16-byte load decode into five 64-wide MFMA slices, and the tile order lets one wave load
+ * the 16 x 64 bytes of a tile as one contiguous kilobyte. */
 int bitnet_packed_bytes(int N, int K, size_t *bytes_out);
 
 /* absmean ternarisation and packing [gptget.net 2402.17764 summary, method; 2B4T write-up
@@ -99,6 +105,21 @@ int hbitlinear_forward(const float *x, int M, int K, int N, int act_bits, int us
                        float *out, const uint8_t *packed_w, float w_scale, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* L independent forwards of one shape in a single call -- e.g. a stack of layers whose
+ * inputs are already held separately, or projections of one block -- each exactly as
+ * hbitlinear_forward (same passages, same arithmetic):
+ *   out[l] = forward(x[l], packed_ws[l], w_scales[l]),  l = 0 .. L-1.
+ * x: L x M x K fp32 (device, contiguous); out: L x M x N fp32 (device, contiguous);
+ * packed_ws: device array of L device pointers to packed N x K weights; w_scales: device
+ * array of L fp32 gammas; workspace: hbitlinear_grouped_workspace_bytes(L, M, K, act_bits)
+ * bytes of device memory.  The call reads packed_ws and w_scales on the device, in stream
+ * order.  Shape rules as hbitlinear_forward, plus 1 <= L <= 65535. */
+int hbitlinear_grouped_workspace_bytes(int L, int M, int K, int act_bits, size_t *bytes_out);
+int hbitlinear_forward_grouped(int L, const float *x, int M, int K, int N, int act_bits,
+                               int use_hadamard, float *out, const uint8_t *const *packed_ws,
+                               const float *w_scales, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* ------------------------------------------------------------------------------------ */
 /* The two stages of the forward, exported so each can be checked and timed on its own.  */
 /* ------------------------------------------------------------------------------------ */
@@ -131,6 +152,13 @@ int bitnet_ternary_gemm_i32(const uint8_t *codes, int M, int K, int N, int act_b
 int hbitlinear_gemm_dequant(const uint8_t *codes, const float *scales, int M, int K, int N,
                             int act_bits, const uint8_t *packed_w, float w_scale, float *out,
                             void *stream);
+
+/* The product stage of hbitlinear_forward_grouped: codes / scales of L*M rows as written by
+ * hbitlinear_quantize on the L x M x K input viewed as (L*M) x K; packed_ws / w_scales device
+ * arrays of L entries; out L x M x N fp32.  All pointers device. */
+int hbitlinear_gemm_dequant_grouped(const uint8_t *codes, const float *scales, int L, int M,
+                                    int K, int N, int act_bits, const uint8_t *const *packed_ws,
+                                    const float *w_scales, float *out, void *stream);
 
 #ifdef __cplusplus
 }

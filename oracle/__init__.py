@@ -50,6 +50,8 @@ def lib():
         L.bitnet_ref_ternarize.argtypes = [P, I, I, P, P]; L.bitnet_ref_ternarize.restype = None
         L.bitnet_ref_row_bytes.argtypes = [I]; L.bitnet_ref_row_bytes.restype = I64
         L.bitnet_ref_packed_bytes.argtypes = [I, I]; L.bitnet_ref_packed_bytes.restype = I64
+        L.bitnet_ref_packed_offset.argtypes = [I, I, I, I]
+        L.bitnet_ref_packed_offset.restype = I64
         L.bitnet_ref_pack.argtypes = [P, I, I, P]; L.bitnet_ref_pack.restype = None
         L.bitnet_ref_unpack.argtypes = [P, I, I, P]; L.bitnet_ref_unpack.restype = I
         L.bitnet_ref_fwht.argtypes = [P, I]; L.bitnet_ref_fwht.restype = None
@@ -118,6 +120,10 @@ def row_bytes(K: int) -> int:
 
 def packed_bytes(N: int, K: int) -> int:
     return int(lib().bitnet_ref_packed_bytes(N, K))
+
+
+def packed_offset(n: int, B: int, b: int, K: int) -> int:
+    return int(lib().bitnet_ref_packed_offset(n, B, b, K))
 
 
 def pack(t):

@@ -9,5 +9,6 @@ from .bitnet import (  # noqa: F401
     BITNET_ERR_UNSUPPORTED, BITNET_ERR_WORKSPACE, BITNET_OK, BitnetError, LIB_PATH,
     bitnet_abi_version, bitnet_pack_weights, bitnet_packed_bytes, bitnet_status_string,
     bitnet_ternary_gemm_i32, bitnet_unpack_weights, hbitlinear_codes_bytes, hbitlinear_forward,
-    hbitlinear_gemm_dequant, hbitlinear_quantize, hbitlinear_workspace_bytes, lib,
+    hbitlinear_forward_grouped, hbitlinear_gemm_dequant, hbitlinear_gemm_dequant_grouped,
+    hbitlinear_grouped_workspace_bytes, hbitlinear_quantize, hbitlinear_workspace_bytes, lib,
 )

@@ -54,6 +54,9 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_quantize": ([P, I, I, I, I, P, P, P, P], I),
             "bitnet_ternary_gemm_i32": ([P, I, I, I, I, P, P, P], I),
             "hbitlinear_gemm_dequant": ([P, P, I, I, I, I, P, F, P, P], I),
+            "hbitlinear_grouped_workspace_bytes": ([I, I, I, I, PSZ], I),
+            "hbitlinear_forward_grouped": ([I, P, I, I, I, I, I, P, P, P, P, SZ, P], I),
+            "hbitlinear_gemm_dequant_grouped": ([P, P, I, I, I, I, I, P, P, P, P], I),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -168,6 +171,40 @@ def hbitlinear_forward(x, N: int, act_bits: int, use_hadamard: bool, packed_w, w
     return out
 
 
+def hbitlinear_grouped_workspace_bytes(L: int, M: int, K: int, act_bits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().hbitlinear_grouped_workspace_bytes(L, M, K, act_bits, ctypes.byref(out)),
+           "hbitlinear_grouped_workspace_bytes")
+    return int(out.value)
+
+
+def hbitlinear_forward_grouped(x, N: int, act_bits: int, use_hadamard: bool, packed_ptrs,
+                               w_scales, out=None, workspace=None, stream=None):
+    """L independent forwards: x (L x M x K fp32), packed_ptrs (int64 device tensor of L
+    device addresses of packed weights), w_scales (L fp32 device tensor) -> out (L x M x N)."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_ptrs, torch.int64, "packed_ptrs")
+    _dev_check(w_scales, torch.float32, "w_scales")
+    L, M, K = x.shape
+    if packed_ptrs.numel() < L or w_scales.numel() < L:
+        raise ValueError("packed_ptrs / w_scales need L entries")
+    if out is None:
+        out = torch.empty((L, M, N), dtype=torch.float32, device=x.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < L * M * N:
+        raise ValueError("out is too small")
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_grouped_workspace_bytes(L, M, K, act_bits),
+                                dtype=torch.uint8, device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward_grouped(L, _ptr(x), M, K, N, act_bits, int(bool(use_hadamard)),
+                                            _ptr(out), _ptr(packed_ptrs), _ptr(w_scales),
+                                            _ptr(workspace), workspace.numel(), _stream(stream)),
+           "hbitlinear_forward_grouped")
+    return out
+
+
 def hbitlinear_quantize(x, act_bits: int, use_hadamard: bool, codes=None, scales=None,
                         want_xh: bool = False, stream=None):
     """Activation stage -> (codes uint8, scales fp32[, xh fp32]) on the device."""
@@ -222,4 +259,27 @@ def hbitlinear_gemm_dequant(codes, scales, M: int, K: int, N: int, act_bits: int
     _check(lib().hbitlinear_gemm_dequant(_ptr(codes), _ptr(scales), M, K, N, act_bits,
                                          _ptr(packed_w), float(w_scale), _ptr(out),
                                          _stream(stream)), "hbitlinear_gemm_dequant")
+    return out
+
+
+def hbitlinear_gemm_dequant_grouped(codes, scales, L: int, M: int, K: int, N: int, act_bits: int,
+                                    packed_ptrs, w_scales, out=None, stream=None):
+    """Product stage of the grouped forward: codes/scales of L*M rows -> out (L x M x N)."""
+    import torch
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    _dev_check(packed_ptrs, torch.int64, "packed_ptrs")
+    _dev_check(w_scales, torch.float32, "w_scales")
+    if codes.numel() < hbitlinear_codes_bytes(L * M, K, act_bits) or scales.numel() < L * M:
+        raise ValueError("codes or scales buffer is too small")
+    if packed_ptrs.numel() < L or w_scales.numel() < L:
+        raise ValueError("packed_ptrs / w_scales need L entries")
+    if out is None:
+        out = torch.empty((L, M, N), dtype=torch.float32, device=codes.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < L * M * N:
+        raise ValueError("out is too small")
+    _check(lib().hbitlinear_gemm_dequant_grouped(_ptr(codes), _ptr(scales), L, M, K, N, act_bits,
+                                                 _ptr(packed_ptrs), _ptr(w_scales), _ptr(out),
+                                                 _stream(stream)), "hbitlinear_gemm_dequant_grouped")
     return out

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
 
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "pack_host.cpp"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "gemm_decode.hip", "pack_host.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

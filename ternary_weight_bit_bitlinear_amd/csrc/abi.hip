@@ -83,8 +83,8 @@ int bitnet_ternary_gemm_i32(const uint8_t* codes, int M, int K, int N, int act_b
     if (codes == nullptr || packed_w == nullptr || acc == nullptr) return BITNET_ERR_NULL;
     int rc = check_shape(M, K, N, act_bits, 0);
     if (rc != BITNET_OK) return rc;
-    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, nullptr, 0.0f, nullptr, acc,
-                                 (hipStream_t)stream));
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, nullptr, nullptr,
+                                 0.0f, nullptr, acc, (hipStream_t)stream));
 }
 
 int hbitlinear_gemm_dequant(const uint8_t* codes, const float* scales, int M, int K, int N,
@@ -95,8 +95,8 @@ int hbitlinear_gemm_dequant(const uint8_t* codes, const float* scales, int M, in
         return BITNET_ERR_NULL;
     int rc = check_shape(M, K, N, act_bits, 0);
     if (rc != BITNET_OK) return rc;
-    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, scales, w_scale, out, nullptr,
-                                 (hipStream_t)stream));
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 w_scale, out, nullptr, (hipStream_t)stream));
 }
 
 int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int use_hadamard,
@@ -113,7 +113,57 @@ int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int us
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
     if (e != hipSuccess) return BITNET_ERR_HIP;
-    return status_of(launch_gemm(codes, M, K, N, act_bits, packed_w, scales, w_scale, out, nullptr, s));
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 w_scale, out, nullptr, s));
+}
+
+int hbitlinear_gemm_dequant_grouped(const uint8_t* codes, const float* scales, int L, int M,
+                                    int K, int N, int act_bits, const uint8_t* const* packed_ws,
+                                    const float* w_scales, float* out, void* stream)
+{
+    if (codes == nullptr || scales == nullptr || packed_ws == nullptr || w_scales == nullptr ||
+        out == nullptr)
+        return BITNET_ERR_NULL;
+    if (L <= 0) return BITNET_ERR_SHAPE;
+    int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    if ((int64_t)L * M > (int64_t)1 << 30 || L > 65535) return BITNET_ERR_UNSUPPORTED;
+    return status_of(launch_gemm(codes, L, M, K, N, act_bits, packed_ws, nullptr, scales, w_scales,
+                                 0.0f, out, nullptr, (hipStream_t)stream));
+}
+
+int hbitlinear_grouped_workspace_bytes(int L, int M, int K, int act_bits, size_t* bytes_out)
+{
+    if (bytes_out == nullptr) return BITNET_ERR_NULL;
+    if (L <= 0) return BITNET_ERR_SHAPE;
+    int rc = check_shape(M, K, 1, act_bits, 0);
+    if (rc != BITNET_OK) return rc;
+    if ((int64_t)L * M > (int64_t)1 << 30) return BITNET_ERR_UNSUPPORTED;
+    *bytes_out = workspace_bytes(L * M, K, act_bits);
+    return BITNET_OK;
+}
+
+int hbitlinear_forward_grouped(int L, const float* x, int M, int K, int N, int act_bits,
+                               int use_hadamard, float* out, const uint8_t* const* packed_ws,
+                               const float* w_scales, void* workspace, size_t workspace_size,
+                               void* stream)
+{
+    if (x == nullptr || out == nullptr || packed_ws == nullptr || w_scales == nullptr)
+        return BITNET_ERR_NULL;
+    if (L <= 0) return BITNET_ERR_SHAPE;
+    int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc != BITNET_OK) return rc;
+    if ((int64_t)L * M > (int64_t)1 << 30 || L > 65535) return BITNET_ERR_UNSUPPORTED;
+    const int rows = L * M;
+    if (workspace == nullptr || workspace_size < workspace_bytes(rows, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(rows, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, rows, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, L, M, K, N, act_bits, packed_ws, nullptr, scales, w_scales,
+                                 0.0f, out, nullptr, s));
 }
 
 }  // extern "C"

@@ -25,9 +25,23 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
                            uint8_t* codes, float* scales, float* xh, hipStream_t stream);
 
-// out_f32 != nullptr: out = (float(acc) * scales[m]) * w_scale;  else acc_i32 receives acc.
-hipError_t launch_gemm(const uint8_t* codes, int M, int K, int N, int bits,
-                       const uint8_t* packed, const float* scales, float w_scale,
-                       float* out_f32, int32_t* acc_i32, hipStream_t stream);
+// Ternary product over L layers of one shape (L = 1 for a single layer).  Layer l reads codes
+// rows [l*M, (l+1)*M), scales[l*M ...], weights wptrs[l] (or w0 when wptrs is null) and
+// wscales[l] (or wscale0), and writes rows [l*M, (l+1)*M) of the output.
+// out_f32 != nullptr: out = (float(acc) * scale[m]) * w_scale;  else acc_i32 receives acc.
+hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                       const uint8_t* const* wptrs, const uint8_t* w0, const float* scales,
+                       const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
+                       hipStream_t stream);
+
+// Kernel variants behind launch_gemm: M <= 16 (gemm_decode.hip) and any M (gemm.hip).
+hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                              const uint8_t* const* wptrs, const uint8_t* w0,
+                              const float* scales, const float* wscales, float wscale0,
+                              float* out_f32, int32_t* acc_i32, hipStream_t stream);
+hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                             const uint8_t* const* wptrs, const uint8_t* w0,
+                             const float* scales, const float* wscales, float wscale0,
+                             float* out_f32, int32_t* acc_i32, hipStream_t stream);
 
 }  // namespace bitnet

@@ -60,12 +60,32 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
     return ((n ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
 }
 
+struct LargeArgs {
+    const uint8_t* codes;          // L x M rows of activation codes
+    const float* scales;           // L x M
+    const uint8_t* const* wptrs;   // device array of L packed weights, or null (then w0)
+    const uint8_t* w0;
+    const float* wscales;          // device array of L weight scales, or null (then wscale0)
+    float wscale0;
+    float* out;                    // L x M x N fp32, or null
+    int32_t* acc;                  // L x M x N int32, or null
+    int M, K, N;
+};
+
 template <int BITS, bool DEQ>
-__global__ __launch_bounds__(NT) void gemm_tern_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ packed, int M, int N, int K,
-    const float* __restrict__ scales, float w_scale, float* __restrict__ out,
-    int32_t* __restrict__ acc_out)
+__global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
 {
+    // Layer blockIdx.z of a grouped call.
+    const int layer = blockIdx.z;
+    const int M = args.M, N = args.N, K = args.K;
+    const int64_t crow_ = BITS == 8 ? (int64_t)K : (int64_t)K / 2;
+    const uint8_t* __restrict__ codes = args.codes + (int64_t)layer * M * crow_;
+    const uint8_t* __restrict__ packed = args.wptrs ? args.wptrs[layer] : args.w0;
+    const float* __restrict__ scales = args.scales ? args.scales + (int64_t)layer * M : nullptr;
+    const float w_scale = args.wscales ? args.wscales[layer] : args.wscale0;
+    float* __restrict__ out = args.out ? args.out + (int64_t)layer * M * N : nullptr;
+    int32_t* __restrict__ acc_out = args.acc ? args.acc + (int64_t)layer * M * N : nullptr;
+
     __shared__ __align__(16) uint8_t As[2][BM * LROW];
     __shared__ __align__(16) uint8_t Bs[2][BN * LROW];
 
@@ -73,17 +93,19 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int nblk = (K + 319) / 320;
-    const int64_t rowb = 64 * (int64_t)nblk;
     const int64_t crow = BITS == 8 ? (int64_t)K : (int64_t)K / 2;
 
-    // Weight rows this thread streams: (tid >> 2) + 64 s, 16-byte chunk (tid & 3) of a block.
-    // Rows past N are clamped: their outputs are never stored.
+    // Weight tiles this thread streams: a block of 16 rows x 64 bytes is one contiguous 1 KB
+    // tile whose 16-byte piece p = 16 c + r holds bytes 16c..16c+15 of row r.  Thread tid takes
+    // piece (tid & 63) of tiles (tid >> 6) + 4 s, s = 0..3; tiles past the last row group are
+    // clamped (their outputs are never stored).
+    const int groups = (N + 15) / 16;
     const uint8_t* bsrc[4];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
-        int n = n0 + (tid >> 2) + 64 * s;
-        n = n < N ? n : N - 1;
-        bsrc[s] = packed + (int64_t)n * rowb + 16 * (tid & 3);
+        int grp = n0 / 16 + (tid >> 6) + 4 * s;
+        grp = grp < groups ? grp : groups - 1;
+        bsrc[s] = packed + (int64_t)grp * nblk * 1024 + 16 * (tid & 63);
     }
     // Activation rows this thread stages.
     constexpr int ACH = BITS == 8 ? 4 : 2;
@@ -105,7 +127,7 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(
     auto load_b = [&](int blk) {
 #pragma unroll
         for (int s = 0; s < 4; s++)
-            bnext[s] = *reinterpret_cast<const uint4*>(bsrc[s] + 64 * (int64_t)blk);
+            bnext[s] = *reinterpret_cast<const uint4*>(bsrc[s] + 1024 * (int64_t)blk);
     };
     uint4 areg[ACH];
     auto load_a = [&](int blk, int i) {
@@ -151,9 +173,10 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(
     };
     auto write_lds = [&](int p) {
         uint8_t* bs = Bs[p];
+        const int prow = (tid >> 6) * 16 + (tid & 15), pcol = 16 * ((tid >> 4) & 3);
 #pragma unroll
         for (int s = 0; s < 4; s++)
-            *reinterpret_cast<uint4*>(bs + ((tid >> 2) + 64 * s) * LROW + 16 * (tid & 3)) =
+            *reinterpret_cast<uint4*>(bs + (prow + 64 * s) * LROW + pcol) =
                 make_uint4(tdw[s][0], tdw[s][1], tdw[s][2], tdw[s][3]);
         uint8_t* as = As[p];
         if constexpr (BITS == 8) {
@@ -252,28 +275,35 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(
     }
 }
 
-template <int BITS, bool DEQ>
-hipError_t launch_large(const uint8_t* codes, int M, int K, int N, const uint8_t* packed,
-                        const float* scales, float w_scale, float* out, int32_t* acc,
-                        hipStream_t s)
+}  // namespace
+
+hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                             const uint8_t* const* wptrs, const uint8_t* w0,
+                             const float* scales, const float* wscales, float wscale0,
+                             float* out_f32, int32_t* acc_i32, hipStream_t stream)
 {
-    dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_tern_kernel<BITS, DEQ>), grid, dim3(NT), 0, s, codes, packed, M, N, K,
-                       scales, w_scale, out, acc);
+    LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N};
+    dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, L);
+    if (out_f32 != nullptr) {
+        if (bits == 8) hipLaunchKernelGGL((gemm_tern_kernel<8, true>), grid, dim3(NT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern_kernel<4, true>), grid, dim3(NT), 0, stream, a);
+    } else {
+        if (bits == 8) hipLaunchKernelGGL((gemm_tern_kernel<8, false>), grid, dim3(NT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern_kernel<4, false>), grid, dim3(NT), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const uint8_t* codes, int M, int K, int N, int bits,
-                       const uint8_t* packed, const float* scales, float w_scale,
-                       float* out_f32, int32_t* acc_i32, hipStream_t stream)
+hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                       const uint8_t* const* wptrs, const uint8_t* w0, const float* scales,
+                       const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
+                       hipStream_t stream)
 {
-    if (out_f32 != nullptr)
-        return bits == 8 ? launch_large<8, true>(codes, M, K, N, packed, scales, w_scale, out_f32, nullptr, stream)
-                         : launch_large<4, true>(codes, M, K, N, packed, scales, w_scale, out_f32, nullptr, stream);
-    return bits == 8 ? launch_large<8, false>(codes, M, K, N, packed, scales, w_scale, nullptr, acc_i32, stream)
-                     : launch_large<4, false>(codes, M, K, N, packed, scales, w_scale, nullptr, acc_i32, stream);
+    if (M <= 16)
+        return launch_gemm_decode(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
+                                  out_f32, acc_i32, stream);
+    return launch_gemm_large(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
+                             out_f32, acc_i32, stream);
 }
 
 }  // namespace bitnet

@@ -1,0 +1,355 @@
+// gemm_decode.hip -- ternary product for decode shapes (M <= 16 tokens) on gfx950, with the
+// dequantisation epilogue fused; one launch can cover L independent layers.
+//
+// Method: BitNet b1.58 2B4T write-up (itdecent.cn), section 1.2 -- the product with {-1,0,+1}
+// weights is exact integer arithmetic; section 1.1 -- five trits per byte, base 3, the first
+// trit most significant.
+//
+// At decode shapes the kernel is bound by the packed weight stream, so each weight byte must
+// be unpacked with as few vector instructions as possible:
+//   - a lane loads the 16 packed bytes (one 16-byte load) that form its part of an MFMA B
+//     operand for one 64-row slab: row n, bytes 16g..16g+15 of a 64-byte block (g = lane/16);
+//   - trits 0..3 of a byte come from one LDS lookup: a table of the 256 byte values, each entry
+//     the four trits as int8, replicated 64 times (one copy per lane, so lookups never
+//     conflict); the lookup address 256*byte + 4*lane is built by one v_perm_b32;
+//   - trit 4 (the least significant digit) is byte mod 3, computed four bytes at a time in
+//     16-bit lanes with floor(x/3) = (85x + 85) >> 8.
+// The MFMA only needs A and B to agree on what each of the 64 k-slots holds, so the slots are
+// arranged around the table: slot (byte b, digit j) for digits 0..3, and the 16 digit-4 trits
+// of a lane in a fifth operand.  The activation operand is permuted to match (a 4 x 4 byte
+// transpose of four 16-code slabs), once per wave and block, shared by the wave's four column
+// tiles.  Pad slabs (k >= K) hold zero trits, so whatever activation codes they meet add 0.
+#include "common.h"
+
+namespace bitnet {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+constexpr int DT = 256;        // threads per workgroup: four waves
+constexpr int WAVE_ROWS = 64;  // weight rows per wave: four 16-row MFMA tiles
+constexpr int WG_ROWS = DT / 64 * WAVE_ROWS;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 3 q in one v_lshl_add_u32 (left to itself the compiler folds w - 3 q into a 64-bit
+// multiply-add, a slow instruction here)
+__device__ __forceinline__ uint32_t times3(uint32_t q)
+{
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, 1, %1" : "=v"(r) : "v"(q));
+    return r;
+}
+
+// trit of the least significant base-3 digit (byte mod 3) of four bytes, as int8
+__device__ __forceinline__ uint32_t trit4(uint32_t w)
+{
+    const uint32_t e = w & 0x00FF00FFu;
+    const uint32_t o = perm(0u, w, 0x0C030C01u);
+    const uint32_t te = __umul24(e, 85u) + 0x00550055u;
+    const uint32_t to = __umul24(o, 85u) + 0x00550055u;
+    const uint32_t q = perm(to, te, 0x07030501u);       // floor(byte / 3), four bytes
+    const uint32_t d = w - times3(q);                    // byte mod 3
+    return perm(0u, 0x000100FFu, d);                     // {0,1,2} -> {-1,0,+1}
+}
+
+// 4 x 4 byte transpose: out[i] = [r0.b_i, r1.b_i, r2.b_i, r3.b_i]
+__device__ __forceinline__ v4i transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3)
+{
+    const uint32_t p01l = perm(r1, r0, 0x05010400u), p01h = perm(r1, r0, 0x07030602u);
+    const uint32_t p23l = perm(r3, r2, 0x05010400u), p23h = perm(r3, r2, 0x07030602u);
+    return v4i{(int)perm(p23l, p01l, 0x05040100u), (int)perm(p23l, p01l, 0x07060302u),
+               (int)perm(p23h, p01h, 0x05040100u), (int)perm(p23h, p01h, 0x07060302u)};
+}
+
+__device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
+{
+    return ((n ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+
+struct DecodeArgs {
+    const uint8_t* codes;          // L x M rows of activation codes
+    const float* scales;           // L x M
+    const uint8_t* const* wptrs;   // device array of L packed weights, or null (then w0)
+    const uint8_t* w0;
+    const float* wscales;          // device array of L weight scales, or null (then wscale0)
+    float wscale0;
+    float* out;                    // L x M x N fp32, or null
+    int32_t* acc;                  // L x M x N int32, or null
+    int L, M, K, N;
+};
+
+constexpr int ASTRIDE = 336;     // LDS bytes per staged activation row: 320 codes + 16 (banks)
+
+// Position in a workgroup's stream of (item, block) steps.  An item is (layer l, chunk c of
+// 256 weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...
+struct StreamPos {
+    int item, B, l, c;
+};
+
+template <int BITS, bool DEQ>
+__global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
+{
+    __shared__ uint32_t lut[256 * 64];
+    __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
+    __shared__ float sbuf[2][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < 256 * 64; i += DT) {
+        const int v = i >> 6;
+        uint32_t e = 0;
+        if (v < 243) {
+            const int d0 = v / 81, d1 = v / 27 % 3, d2 = v / 9 % 3, d3 = v / 3 % 3;
+            e = (uint32_t)(uint8_t)(d0 - 1) | (uint32_t)(uint8_t)(d1 - 1) << 8 |
+                (uint32_t)(uint8_t)(d2 - 1) << 16 | (uint32_t)(uint8_t)(d3 - 1) << 24;
+        }
+        lut[i] = e;
+    }
+
+    const int K = a.K, N = a.N, M = a.M;
+    const int nblk = (K + 319) / 320;
+    const int crow = BITS == 8 ? K : K / 2;            // code bytes per activation row
+    const int groups = (N + 15) / 16;                   // 16-row weight groups (tiles per block)
+    const int nchunk = (N + WG_ROWS - 1) / WG_ROWS;
+    const int items = a.L * nchunk;
+    const int my_items = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int total = my_items * nblk;
+    if (total == 0) return;
+    const uint32_t laneoff = 4u * (uint32_t)lane;
+    const int g = lane >> 4;
+
+    auto start = [&](StreamPos& p, int item) {
+        p.item = item;
+        p.B = 0;
+        p.l = item / nchunk;
+        p.c = item - p.l * nchunk;
+    };
+    auto advance = [&](StreamPos& p) {
+        if (++p.B == nblk) start(p, p.item + (int)gridDim.x);
+    };
+
+    // ---- weights: one 1 KB tile (16 rows x 64 bytes) per MFMA column tile and block; the
+    // tile's 16-byte pieces are in lane order, so lane l reads piece l.  Buffer loads: rows
+    // past the last 16-row group read as zero (their outputs are not stored).
+    const uint32_t tile_bytes = 1024u * (uint32_t)nblk;         // one 16-row group
+    uint32_t w_off[4];
+#pragma unroll
+    for (int f = 0; f < 4; f++) w_off[f] = (uint32_t)(wave * 4 + f) * tile_bytes + 16u * lane;
+    auto load_w = [&](u4 (&dst)[4], const StreamPos& p) {
+        const uint8_t* W = a.wptrs ? a.wptrs[p.l] : a.w0;
+        const int g0 = p.c * (WG_ROWS / 16);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(W + (int64_t)g0 * tile_bytes), 0, (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
+#pragma unroll
+        for (int f = 0; f < 4; f++) dst[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)w_off[f], 1024 * p.B, 0);
+    };
+
+    // ---- activations: the workgroup stages the 16 rows x 320 codes of a block in LDS with
+    // coalesced loads (rows past M read as zero; slabs past K meet zero trits), plus the 16
+    // activation scales of the item.
+    constexpr int ACH = BITS == 8 ? 20 : 10;            // 16-byte chunks per row and block
+    const int q0 = tid, q1 = tid + DT;                  // this thread's chunks (q1 only if < 16*ACH)
+    const bool has_q0 = q0 < 16 * ACH, has_q1 = q1 < 16 * ACH;
+    const uint32_t aoff0 = (uint32_t)(q0 / ACH) * (uint32_t)crow + 16u * (q0 % ACH);
+    const uint32_t aoff1 = (uint32_t)(q1 / ACH) * (uint32_t)crow + 16u * (q1 % ACH);
+    u4 ar0 = u4{0, 0, 0, 0}, ar1 = u4{0, 0, 0, 0};
+    float sr = 0.0f;
+    auto load_a = [&](const StreamPos& p) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.codes + (int64_t)p.l * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
+        const int kb = (BITS == 8 ? 320 : 160) * p.B;
+        if (has_q0) ar0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff0, kb, 0);
+        if (has_q1) ar1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff1, kb, 0);
+        if constexpr (DEQ) {
+            if (tid < 16) {
+                const auto ss = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
+                sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * tid, 0, 0));
+            }
+        }
+    };
+    auto stage_a = [&](int buf, u4 v0, u4 v1, float sv) {
+        auto put = [&](u4 v, int q) {
+            uint8_t* row = abuf[buf] + (q / ACH) * ASTRIDE;
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<u4*>(row + 16 * (q % ACH)) = v;
+            } else {
+                u4 lo = u4{sext_nibbles(v[0] & 0x0F0F0F0Fu), sext_nibbles((v[0] >> 4) & 0x0F0F0F0Fu),
+                           sext_nibbles(v[1] & 0x0F0F0F0Fu), sext_nibbles((v[1] >> 4) & 0x0F0F0F0Fu)};
+                u4 hi = u4{sext_nibbles(v[2] & 0x0F0F0F0Fu), sext_nibbles((v[2] >> 4) & 0x0F0F0F0Fu),
+                           sext_nibbles(v[3] & 0x0F0F0F0Fu), sext_nibbles((v[3] >> 4) & 0x0F0F0F0Fu)};
+                *reinterpret_cast<u4*>(row + 32 * (q % ACH)) = lo;
+                *reinterpret_cast<u4*>(row + 32 * (q % ACH) + 16) = hi;
+            }
+        };
+        if (has_q0) put(v0, q0);
+        if (has_q1) put(v1, q1);
+        if (DEQ && tid < 16) sbuf[buf][tid] = sv;
+    };
+
+    auto lookup = [&](uint32_t w, uint32_t sel) -> int {
+        const uint32_t addr = perm(w, laneoff, sel);    // 256 * byte + 4 * lane
+        return (int)*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lut) + addr);
+    };
+    auto lookups = [&](const u4& w, v4i (&b)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            b[u] = v4i{lookup(w[u], 0x0C0C0400u), lookup(w[u], 0x0C0C0500u),
+                       lookup(w[u], 0x0C0C0600u), lookup(w[u], 0x0C0C0700u)};
+    };
+
+    v4i acc[4];
+#pragma unroll
+    for (int f = 0; f < 4; f++) acc[f] = v4i{0, 0, 0, 0};
+
+    // One block of one item: table lookups go out two column tiles at a time, ahead of the
+    // MFMAs that consume them.
+    auto compute = [&](const u4 (&w)[4], int buf) {
+        v4i b0[4], b1[4];
+        lookups(w[0], b0);
+        lookups(w[1], b1);
+        const uint8_t* ar = abuf[buf] + (lane & 15) * ASTRIDE + 16 * g;
+        u4 d[5];
+#pragma unroll
+        for (int j = 0; j < 5; j++) d[j] = *reinterpret_cast<const u4*>(ar + 64 * j);
+        v4i a1[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) a1[u] = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);
+        const v4i a5 = v4i{(int)d[4][0], (int)d[4][1], (int)d[4][2], (int)d[4][3]};
+        v4i t4[4];
+#pragma unroll
+        for (int f = 0; f < 4; f++)
+            t4[f] = v4i{(int)trit4(w[f][0]), (int)trit4(w[f][1]), (int)trit4(w[f][2]), (int)trit4(w[f][3])};
+#pragma unroll
+        for (int u = 0; u < 4; u++) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b0[u], acc[0], 0, 0, 0);
+        lookups(w[2], b0);
+#pragma unroll
+        for (int u = 0; u < 4; u++) acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b1[u], acc[1], 0, 0, 0);
+        lookups(w[3], b1);
+#pragma unroll
+        for (int f = 0; f < 2; f++) acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a5, t4[f], acc[f], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; u++) acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b0[u], acc[2], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; u++) acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b1[u], acc[3], 0, 0, 0);
+#pragma unroll
+        for (int f = 2; f < 4; f++) acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a5, t4[f], acc[f], 0, 0, 0);
+    };
+
+    // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
+    // column l & 15.
+    auto finish = [&](const StreamPos& p, int buf) {
+        const float wsc = a.wscales ? a.wscales[p.l] : a.wscale0;
+        const int nbase = p.c * WG_ROWS + wave * WAVE_ROWS + (lane & 15);
+        const int64_t obase = (int64_t)p.l * M * N;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int mo = 4 * g + r;
+            const float sx = DEQ ? sbuf[buf][mo] : 0.0f;
+            if (mo < M) {
+#pragma unroll
+                for (int f = 0; f < 4; f++) {
+                    const int n = nbase + 16 * f;
+                    if (n < N) {
+                        const uint32_t o = (uint32_t)mo * (uint32_t)N + (uint32_t)n;
+                        if constexpr (DEQ)
+                            a.out[obase + o] = ((float)acc[f][r] * sx) * wsc;
+                        else
+                            a.acc[obase + o] = acc[f][r];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 4; f++) acc[f] = v4i{0, 0, 0, 0};
+    };
+
+    // Pipeline: weights run three steps ahead (a four-slot register ring); activations are
+    // loaded two steps ahead into registers and staged into LDS one step ahead.  Loads are
+    // unconditional -- past the last step the positions stay put -- so that no branch separates
+    // a load from its use.
+    StreamPos pc, pa, pw;
+    start(pc, blockIdx.x);
+    pa = pc;
+    pw = pc;
+    u4 w0[4], w1[4], w2[4], w3[4];
+    load_w(w0, pw);
+    if (1 < total) advance(pw);
+    load_w(w1, pw);
+    if (2 < total) advance(pw);
+    load_w(w2, pw);
+    load_a(pa);                                     // activations of step 0
+    stage_a(0, ar0, ar1, sr);
+    if (1 < total) advance(pa);
+    load_a(pa);                                     // activations of step 1
+    __syncthreads();                                // table and step 0 activations in LDS
+
+    auto step = [&](const u4 (&w)[4], u4 (&wpre)[4], int t) {
+        const u4 n0 = ar0, n1 = ar1;                // activations of step t + 1
+        const float ns = sr;
+        if (t + 2 < total) advance(pa);
+        load_a(pa);                                 // activations of step t + 2
+        if (t + 3 < total) advance(pw);
+        load_w(wpre, pw);                           // weights of step t + 3
+        compute(w, t & 1);
+        stage_a((t + 1) & 1, n0, n1, ns);
+        if (pc.B == nblk - 1) finish(pc, t & 1);
+        advance(pc);
+        __syncthreads();
+    };
+    for (int t = 0; t < total; t += 4) {
+        step(w0, w3, t);
+        if (t + 1 >= total) break;
+        step(w1, w0, t + 1);
+        if (t + 2 >= total) break;
+        step(w2, w1, t + 2);
+        if (t + 3 >= total) break;
+        step(w3, w2, t + 3);
+    }
+}
+
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
+                              const uint8_t* const* wptrs, const uint8_t* w0,
+                              const float* scales, const float* wscales, float wscale0,
+                              float* out_f32, int32_t* acc_i32, hipStream_t stream)
+{
+    // Buffer ranges and lane offsets are 32-bit: one weight matrix and one layer's codes must
+    // stay below 2 GiB.
+    const int64_t packed = (int64_t)((N + 15) / 16) * 16 * 64 * ((K + 319) / 320);
+    if (packed >= ((int64_t)1 << 31) || (int64_t)M * K >= ((int64_t)1 << 31) ||
+        (int64_t)M * N >= ((int64_t)1 << 32))
+        return hipErrorInvalidValue;
+    DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N};
+    const int items = L * ((N + WG_ROWS - 1) / WG_ROWS);
+    const int grid = items < 2 * device_cus() ? items : 2 * device_cus();
+    if (out_f32 != nullptr) {
+        if (bits == 8) hipLaunchKernelGGL((gemm_decode_kernel<8, true>), dim3(grid), dim3(DT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_decode_kernel<4, true>), dim3(grid), dim3(DT), 0, stream, a);
+    } else {
+        if (bits == 8) hipLaunchKernelGGL((gemm_decode_kernel<8, false>), dim3(grid), dim3(DT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_decode_kernel<4, false>), dim3(grid), dim3(DT), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -17,6 +17,16 @@ constexpr int kBlock = 320;  // weights per 64-byte block of a packed row
 
 int64_t packed_row_bytes(int K) { return 64 * (int64_t)((K + kBlock - 1) / kBlock); }
 
+// Rows go in groups of 16; group G and block B form one 1024-byte tile, in which byte b of
+// row n sits at ((b / 16) * 16 + n % 16) * 16 + b % 16.  One wave can then load the 16 rows x
+// 64 bytes of a tile as one contiguous kilobyte.
+inline int64_t tile_offset(int n, int B, int b, int nblk)
+{
+    return ((int64_t)(n / 16) * nblk + B) * 1024 + (int64_t)((b / 16) * 16 + n % 16) * 16 + b % 16;
+}
+
+int64_t padded_rows(int N) { return (int64_t)(N + 15) / 16 * 16; }
+
 int check_nk(int N, int K)
 {
     if (N <= 0 || K <= 0) return BITNET_ERR_SHAPE;
@@ -40,7 +50,7 @@ int bitnet_packed_bytes(int N, int K, size_t* bytes_out)
     if (bytes_out == nullptr) return BITNET_ERR_NULL;
     int rc = check_nk(N, K);
     if (rc != BITNET_OK) return rc;
-    *bytes_out = (size_t)N * (size_t)packed_row_bytes(K);
+    *bytes_out = (size_t)padded_rows(N) * (size_t)packed_row_bytes(K);
     return BITNET_OK;
 }
 
@@ -56,21 +66,20 @@ int bitnet_pack_weights(const float* W, int N, int K, uint8_t* packed, float* w_
     const float gamma = (float)(sum / (double)count);
     *w_scale_out = gamma;
 
-    const int64_t rb = packed_row_bytes(K);
     const int nblk = (K + kBlock - 1) / kBlock;
-    for (int n = 0; n < N; n++) {
-        const float* wr = W + (int64_t)n * K;
-        uint8_t* pr = packed + (int64_t)n * rb;
+    for (int n = 0; n < padded_rows(N); n++) {
+        const float* wr = n < N ? W + (int64_t)n * K : W;
         for (int blk = 0; blk < nblk; blk++) {
             for (int b = 0; b < 64; b++) {
-                // byte b of the block: weights k = 320 blk + b + 64 i as digit i, MSB first
+                // byte b of the block: weights k = 320 blk + b + 64 i as digit i, MSB first;
+                // pad rows (n >= N) and pad columns (k >= K) are zero weights
                 int v = 0;
                 for (int i = 0; i < 5; i++) {
                     const int k = kBlock * blk + b + 64 * i;
-                    const int t = (k < K && gamma != 0.0f) ? ternary(wr[k], gamma) : 0;
+                    const int t = (n < N && k < K && gamma != 0.0f) ? ternary(wr[k], gamma) : 0;
                     v = 3 * v + (t + 1);
                 }
-                pr[64 * blk + b] = (uint8_t)v;
+                packed[tile_offset(n, blk, b, nblk)] = (uint8_t)v;
             }
         }
     }
@@ -82,22 +91,20 @@ int bitnet_unpack_weights(const uint8_t* packed, int N, int K, int8_t* trits)
     if (packed == nullptr || trits == nullptr) return BITNET_ERR_NULL;
     int rc = check_nk(N, K);
     if (rc != BITNET_OK) return rc;
-    const int64_t rb = packed_row_bytes(K);
     const int nblk = (K + kBlock - 1) / kBlock;
     // Two passes: check every byte first, so a malformed buffer leaves trits untouched.
     for (int pass = 0; pass < 2; pass++) {
-        for (int n = 0; n < N; n++) {
-            const uint8_t* pr = packed + (int64_t)n * rb;
+        for (int n = 0; n < padded_rows(N); n++) {
             int8_t* tr = trits + (int64_t)n * K;
             for (int blk = 0; blk < nblk; blk++) {
                 for (int b = 0; b < 64; b++) {
-                    int v = pr[64 * blk + b];
+                    int v = packed[tile_offset(n, blk, b, nblk)];
                     if (v > 242) return BITNET_ERR_FORMAT;
                     for (int i = 4; i >= 0; i--) {  // least significant digit is i = 4
                         const int d = v % 3;
                         v /= 3;
                         const int k = kBlock * blk + b + 64 * i;
-                        if (k >= K) {
+                        if (n >= N || k >= K) {
                             if (d != 1) return BITNET_ERR_FORMAT;
                         } else if (pass == 1) {
                             tr[k] = (int8_t)(d - 1);

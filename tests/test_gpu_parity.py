@@ -269,3 +269,50 @@ def test_forward_rejects_small_workspace(tb):
         tb.hbitlinear_forward(dev(np.ones((M, K), np.float32)), N, 8, True, dev(packed), g,
                               workspace=ws)
     assert e.value.status == tb.BITNET_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------- grouped calls ----
+
+@pytest.mark.parametrize("L,M,K,N,bits,had", [(5, 16, 4096, 512, 8, False), (3, 1, 1024, 300, 8, True),
+                                              (4, 40, 4096, 256, 4, True), (2, 7, 960, 100, 4, False)])
+def test_forward_grouped_matches_oracle(tb, L, M, K, N, bits, had):
+    say(f"  grouped L={L} M={M} K={K} N={N} bits={bits} had={had}")
+    x = si.normal(si.seed_for(8, 0) + K + M, L * M * K).reshape(L, M, K)
+    x[0, 0] = 0.0
+    packs, gs, ts = [], [], []
+    for l in range(L):
+        packed, g = tb.bitnet_pack_weights(si.gaussian_weights(8, N, K, layer=l))
+        packs.append(dev(packed)); gs.append(g); ts.append(oracle.unpack(packed, N, K))
+    ptrs = torch.tensor([p.data_ptr() for p in packs], dtype=torch.int64, device="cuda")
+    wsc = torch.tensor(gs, dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    y = tb.hbitlinear_forward_grouped(xd, N, bits, had, ptrs, wsc)
+    # the product stage on its own, from the activation stage's codes
+    codes, scales = tb.hbitlinear_quantize(xd.view(L * M, K), bits, had)
+    y2 = tb.hbitlinear_gemm_dequant_grouped(codes, scales, L, M, K, N, bits, ptrs, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for l in range(L):
+        yl = tb.hbitlinear_forward(xd[l].contiguous(), N, bits, had, packs[l], gs[l])
+        torch.cuda.synchronize()
+        assert torch.equal(y[l], yl), f"layer {l} differs from its single call"
+        oq, os_ = oracle.quantize(x[l], bits, had)
+        oy = oracle.epilogue(oracle.gemm(oq, ts[l]), os_, np.float32(gs[l]))
+        gq = codes_to_int8(codes, L * M, K, bits)[l * M:(l + 1) * M]
+        match = np.all(gq == oq, axis=1)
+        np.testing.assert_array_equal(y[l].cpu().numpy()[match], oy[match])
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_decode_kernel_gemm_i32(tb, M, bits):
+    # M <= 16 runs the decode-shape kernel: check it bit-exactly on shared codes, with a ragged N
+    K, N = 4096, 4096 + 80
+    qp = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(M + bits)
+    q = rng.integers(-qp - 1, qp + 1, size=(M, K)).astype(np.int8)
+    packed, _ = tb.bitnet_pack_weights(si.gaussian_weights(9, N, K))
+    cb = q.view(np.uint8) if bits == 8 else oracle.pack_int4(q)
+    acc = tb.bitnet_ternary_gemm_i32(dev(cb.reshape(-1)), M, K, N, bits, dev(packed))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.gemm(q, oracle.unpack(packed, N, K)))
