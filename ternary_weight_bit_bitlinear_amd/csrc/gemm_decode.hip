@@ -96,7 +96,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
     __shared__ uint32_t lut[256 * 64];
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
-    __shared__ float sbuf[2][16];
+    __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < 256 * 64; i += DT) {
@@ -156,23 +156,29 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     const bool has_q0 = q0 < 16 * ACH, has_q1 = q1 < 16 * ACH;
     const uint32_t aoff0 = (uint32_t)(q0 / ACH) * (uint32_t)crow + 16u * (q0 % ACH);
     const uint32_t aoff1 = (uint32_t)(q1 / ACH) * (uint32_t)crow + 16u * (q1 % ACH);
-    u4 ar0 = u4{0, 0, 0, 0}, ar1 = u4{0, 0, 0, 0};
-    float sr = 0.0f;
-    auto load_a = [&](const StreamPos& p) {
+    struct ASlot {
+        u4 v0, v1;       // this thread's one or two 16-byte chunks of codes
+        float s;         // threads 0..15: activation scale of row tid
+        float ws;        // weight scale of the layer (uniform)
+    };
+    // Branch-free loads: a thread without a chunk reads at an offset past the buffer range,
+    // which returns zeros.
+    const uint32_t kOut = 0x7FFFFFF0u;
+    const uint32_t aoff0x = has_q0 ? aoff0 : kOut, aoff1x = has_q1 ? aoff1 : kOut;
+    auto load_a = [&](ASlot& dst, const StreamPos& p) {
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (int64_t)p.l * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
         const int kb = (BITS == 8 ? 320 : 160) * p.B;
-        if (has_q0) ar0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff0, kb, 0);
-        if (has_q1) ar1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff1, kb, 0);
+        dst.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff0x, kb, 0);
+        dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff1x, kb, 0);
         if constexpr (DEQ) {
-            if (tid < 16) {
-                const auto ss = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
-                sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * tid, 0, 0));
-            }
+            const auto ss = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
+            dst.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * (tid & 15), 0, 0));
+            dst.ws = a.wscales ? a.wscales[p.l] : a.wscale0;
         }
     };
-    auto stage_a = [&](int buf, u4 v0, u4 v1, float sv) {
+    auto stage_a = [&](int buf, const ASlot& x) {
         auto put = [&](u4 v, int q) {
             uint8_t* row = abuf[buf] + (q / ACH) * ASTRIDE;
             if constexpr (BITS == 8) {
@@ -186,9 +192,10 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
                 *reinterpret_cast<u4*>(row + 32 * (q % ACH) + 16) = hi;
             }
         };
-        if (has_q0) put(v0, q0);
-        if (has_q1) put(v1, q1);
-        if (DEQ && tid < 16) sbuf[buf][tid] = sv;
+        if (has_q0) put(x.v0, q0);
+        if (has_q1) put(x.v1, q1);
+        if (DEQ && tid < 16) sbuf[buf][tid] = x.s;
+        if (DEQ && tid == 16) sbuf[buf][16] = x.ws;
     };
 
     auto lookup = [&](uint32_t w, uint32_t sel) -> int {
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
     // column l & 15.
     auto finish = [&](const StreamPos& p, int buf) {
-        const float wsc = a.wscales ? a.wscales[p.l] : a.wscale0;
+        const float wsc = DEQ ? sbuf[buf][16] : 0.0f;
         const int nbase = p.c * WG_ROWS + wave * WAVE_ROWS + (lane & 15);
         const int64_t obase = (int64_t)p.l * M * N;
 #pragma unroll
@@ -269,46 +276,47 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     };
 
     // Pipeline: weights run three steps ahead (a four-slot register ring); activations are
-    // loaded two steps ahead into registers and staged into LDS one step ahead.  Loads are
-    // unconditional -- past the last step the positions stay put -- so that no branch separates
-    // a load from its use.
+    // loaded three steps ahead into registers and staged into LDS one step ahead.  Waiting for
+    // a load also waits for every load issued before it, so the activations of step t + 1
+    // (staged during step t) must have been issued no later than the weights of step t + 1.
+    // Loads are unconditional -- past the last step the positions stay put -- so that no
+    // branch separates a load from its use.
     StreamPos pc, pa, pw;
     start(pc, blockIdx.x);
     pa = pc;
     pw = pc;
-    u4 w0[4], w1[4], w2[4], w3[4];
+    u4 w0[4], w1[4], w2[4], w3[4];                  // weight ring
+    ASlot x0, x1, x2, x3;                           // activation ring
+    load_a(x0, pa);                                 // step 0
     load_w(w0, pw);
-    if (1 < total) advance(pw);
+    stage_a(0, x0);
+    if (1 < total) { advance(pa); advance(pw); }
+    load_a(x1, pa);                                 // step 1
     load_w(w1, pw);
-    if (2 < total) advance(pw);
+    if (2 < total) { advance(pa); advance(pw); }
+    load_a(x2, pa);                                 // step 2
     load_w(w2, pw);
-    load_a(pa);                                     // activations of step 0
-    stage_a(0, ar0, ar1, sr);
-    if (1 < total) advance(pa);
-    load_a(pa);                                     // activations of step 1
     __syncthreads();                                // table and step 0 activations in LDS
 
-    auto step = [&](const u4 (&w)[4], u4 (&wpre)[4], int t) {
-        const u4 n0 = ar0, n1 = ar1;                // activations of step t + 1
-        const float ns = sr;
-        if (t + 2 < total) advance(pa);
-        load_a(pa);                                 // activations of step t + 2
-        if (t + 3 < total) advance(pw);
-        load_w(wpre, pw);                           // weights of step t + 3
+    // Step t: loads for step t + 3, MFMAs of step t, staging of step t + 1.
+    auto step = [&](const u4 (&w)[4], u4 (&wpre)[4], const ASlot& xnext, ASlot& xpre, int t) {
+        if (t + 3 < total) { advance(pa); advance(pw); }
+        load_a(xpre, pa);
+        load_w(wpre, pw);
         compute(w, t & 1);
-        stage_a((t + 1) & 1, n0, n1, ns);
+        stage_a((t + 1) & 1, xnext);
         if (pc.B == nblk - 1) finish(pc, t & 1);
         advance(pc);
         __syncthreads();
     };
     for (int t = 0; t < total; t += 4) {
-        step(w0, w3, t);
+        step(w0, w3, x1, x3, t);
         if (t + 1 >= total) break;
-        step(w1, w0, t + 1);
+        step(w1, w0, x2, x0, t + 1);
         if (t + 2 >= total) break;
-        step(w2, w1, t + 2);
+        step(w2, w1, x3, x1, t + 2);
         if (t + 3 >= total) break;
-        step(w3, w2, t + 3);
+        step(w3, w2, x0, x2, t + 3);
     }
 }
 
