@@ -42,8 +42,21 @@ def parse_args():
     p.add_argument("--large-steps", type=int, default=10)
     p.add_argument("--no-large", action="store_true", help="skip the large-M workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["decode", "wo", "wdown", "block"], default=None,
-                   help="run one workload only (profiling)")
+    p.add_argument("--only", choices=["headline", "decode", "wo", "wdown", "block"], default=None,
+                   help="run one workload only (profiling); 'headline' is the grouped decode "
+                        "launch alone, without the sequential and other-M decode runs")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device-to-device copy of --copy-mib MiB five times "
+                        "(the reference point for the HBM byte counters)")
+    p.add_argument("--copy-mib", type=int, default=1024)
+    p.add_argument("--summarize-counters", metavar="DIR", default=None,
+                   help="write the HBM-traffic summary from the four counter runs under DIR "
+                        "(fetch/, write/, cal_fetch/, cal_write/) to --out")
+    p.add_argument("--summarize-trace", metavar="DIR", default=None,
+                   help="write the kernel-trace statistics found under DIR to --out")
+    p.add_argument("--kernel", default="gemm_decode_kernel")
+    p.add_argument("--command", default="", help="command line recorded in a summary")
+    p.add_argument("--out", default=None)
     return p.parse_args()
 
 
@@ -189,6 +202,142 @@ def cpu_baseline_decode(si, oracle, d, tb, layers=2):
                        f"product + epilogue per layer), {dt:.1f} s")
 
 
+# ------------------------------------------------------------- counters and traces ----
+
+# kernel name prefix -> the sources it is compiled from (a counter summary is void once they change)
+KERNEL_SOURCES = {
+    "gemm_decode_kernel": ["gemm_decode.hip", "common.h"],
+    "gemm_tern_kernel": ["gemm.hip", "common.h"],
+    "quantize_rows_kernel": ["quant.hip", "common.h"],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "ternary_weight_bit_bitlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of `mib` MiB, five times: each launch reads and writes
+    exactly mib MiB, which fixes the scale of the HBM byte counters."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(0)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert int(dst[n - 1]) == 7
+    return {"copy_bytes_per_launch": n, "launches": 5}
+
+
+def _counter_means(d, kernel_prefix, counter):
+    """Mean per dispatch of `counter` over the dispatches of kernels whose name holds
+    `kernel_prefix` (values of one dispatch summed over its instances)."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_prefix in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    key = (f, r["Dispatch_Id"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} values for {kernel_prefix} under {d}")
+    return per
+
+
+def summarize_counters(args):
+    """HBM bytes per launch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the plain copy of known size."""
+    d = args.summarize_counters
+    fetch = list(_counter_means(os.path.join(d, "fetch"), args.kernel, "FETCH_SIZE").values())
+    write = list(_counter_means(os.path.join(d, "write"), args.kernel, "WRITE_SIZE").values())
+    cal_f = _counter_means(os.path.join(d, "cal_fetch"), COPY_KERNEL, "FETCH_SIZE")
+    cal_w = _counter_means(os.path.join(d, "cal_write"), COPY_KERNEL, "WRITE_SIZE")
+    copy_bytes = args.copy_mib << 20
+    # the five big copies are the largest copy dispatches of the calibration run
+    cf = sorted(cal_f.values())[-5:]
+    cw = sorted(cal_w.values())[-5:]
+    f_scale = copy_bytes / (1024.0 * sum(cf) / len(cf))
+    w_scale = copy_bytes / (1024.0 * sum(cw) / len(cw))
+    f_kib = sum(fetch) / len(fetch)
+    w_kib = sum(write) / len(write)
+    traffic = 1024.0 * (f_kib * f_scale + w_kib * w_scale)
+    lines = [
+        f"# HBM traffic of {args.kernel}: rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated",
+        f"kernel: {args.kernel}",
+        f"source_digest: {source_digest(args.kernel)}",
+        f"dispatches_fetch: {len(fetch)}",
+        f"dispatches_write: {len(write)}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"copy_bytes_per_dispatch: {copy_bytes}",
+        f"copy_fetch_kib_per_dispatch: {sum(cf) / len(cf):.1f}",
+        f"copy_write_kib_per_dispatch: {sum(cw) / len(cw):.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        "commands:",
+    ] + ["  " + c for c in args.command.split(" ;; ") if c]
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text, end="")
+
+
+def summarize_trace(args):
+    """The per-kernel statistics table of a rocprofv3 --kernel-trace --stats run, as text."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"),
+                             recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.summarize_trace}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append(r)
+    lines = ["# rocprofv3 --kernel-trace --stats summary", "command:"]
+    lines += ["  " + c for c in args.command.split(" ;; ") if c]
+    lines.append("")
+    lines.append(f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):7.2f}  {name}")
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text, end="")
+
+
+def recorded_traffic(kernel, workload):
+    """traffic_bytes_per_launch from the committed counter summary of `kernel` on `workload`,
+    or None when there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest(kernel):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 # -------------------------------------------------------------------------- large M ----
 
 def run_large(torch, tb, si, config, steps, warmup):
@@ -262,6 +411,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this build has no multi-GPU path.", flush=True)
         sys.exit(2)
+    if args.summarize_counters:
+        return summarize_counters(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
 
     import numpy as np  # noqa: F401
     import torch
@@ -271,23 +424,27 @@ def main():
     tb.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(torch, args.copy_mib)), flush=True)
+        return
 
     result = {}
-    if args.only in (None, "decode"):
+    if args.only in (None, "decode", "headline"):
         log(f"[bench] decode: preparing M={args.M}, {args.layers} layers")
         d = make_decode(torch, tb, si, args.M, args.layers)
         log("[bench] decode: timing (grouped)")
         r = run_decode_grouped(torch, tb, d, args.steps, args.warmup)
         log(f"[bench] decode grouped: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.1f} us "
             f"({r['gemm_gbs']:.0f} GB/s), quant {r['quant_us']:.1f} us")
-        rs = run_decode(torch, tb, d, max(2, args.steps // 4), 1)
-        log(f"[bench] decode sequential: {rs['tokens_per_s']:.4g} tokens/s, gemm {rs['gemm_us']:.2f} us "
-            f"per layer ({rs['gemm_gbs']:.0f} GB/s)")
-        sequential = dict(tokens_per_s=rs["tokens_per_s"], gemm_us_per_layer=rs["gemm_us"],
-                          quant_us_per_layer=rs["quant_us"], gemm_gbs=rs["gemm_gbs"],
-                          hbm_frac=rs["gemm_gbs"] / HBM_PEAK_GBS)
-        others = {}
-        for m in (1, 4):
+        sequential, others = None, {}
+        if args.only != "headline":
+            rs = run_decode(torch, tb, d, max(2, args.steps // 4), 1)
+            log(f"[bench] decode sequential: {rs['tokens_per_s']:.4g} tokens/s, gemm "
+                f"{rs['gemm_us']:.2f} us per layer ({rs['gemm_gbs']:.0f} GB/s)")
+            sequential = dict(tokens_per_s=rs["tokens_per_s"], gemm_us_per_layer=rs["gemm_us"],
+                              quant_us_per_layer=rs["quant_us"], gemm_gbs=rs["gemm_gbs"],
+                              hbm_frac=rs["gemm_gbs"] / HBM_PEAK_GBS)
+        for m in ((1, 4) if args.only != "headline" else ()):
             dm = make_decode(torch, tb, si, m, args.layers)
             rm = run_decode_grouped(torch, tb, dm, max(2, args.steps // 2), 1)
             others[f"M{m}"] = dict(tokens_per_s=rm["tokens_per_s"], gemm_us=rm["gemm_us"],
@@ -296,10 +453,12 @@ def main():
                 f"{rm['gemm_us']:.1f} us ({rm['gemm_gbs']:.0f} GB/s)")
             del dm
         cpu = None
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and args.only != "headline":
             import oracle
             log("[bench] cpu baseline (oracle)")
             cpu = cpu_baseline_decode(si, oracle, d, tb)
+        workload = f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_grouped_L{d['L']}"
+        traffic = recorded_traffic("gemm_decode_kernel", f"M{d['M']}_L{d['L']}")
         result = {
             "metric": METRIC,
             "value": r["tokens_per_s"],
@@ -313,7 +472,7 @@ def main():
             "vs_baseline": None,
             "dtype": "int8",
             "data": "synthetic",
-            "config": {"workload": f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_grouped_L{d['L']}",
+            "config": {"workload": workload,
                        "M": d["M"], "K": 4096, "N": 4096, "layers": d["L"], "act_bits": 8,
                        "use_hadamard": False,
                        "step": "activation stage over L*M rows + one grouped product launch over "
@@ -321,7 +480,7 @@ def main():
                        "tokens_per_s": "M * layers * steps / seconds (a token counts once per layer)"},
             "int_tops": r["int_tops"],
             "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                          "kernel": "gemm_decode_kernel<8,true>", "launch_us": r["gemm_us"],
                          "algorithmic_bytes_per_launch": r["gemm_bytes"]},
             "quant_kernel_us": r["quant_us"],
