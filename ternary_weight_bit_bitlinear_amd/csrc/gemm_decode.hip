@@ -7,18 +7,19 @@
 //
 // At decode shapes the kernel is bound by the packed weight stream, so each weight byte must
 // be unpacked with as few vector instructions as possible:
-//   - a lane loads the 16 packed bytes (one 16-byte load) that form its part of an MFMA B
-//     operand for one 64-row slab: row n, bytes 16g..16g+15 of a 64-byte block (g = lane/16);
-//   - trits 0..3 of a byte come from one LDS lookup: a table of the 256 byte values, each entry
-//     the four trits as int8, replicated 64 times (one copy per lane, so lookups never
-//     conflict); the lookup address 256*byte + 4*lane is built by one v_perm_b32;
-//   - trit 4 (the least significant digit) is byte mod 3, computed four bytes at a time in
-//     16-bit lanes with floor(x/3) = (85x + 85) >> 8.
-// The MFMA only needs A and B to agree on what each of the 64 k-slots holds, so the slots are
-// arranged around the table: slot (byte b, digit j) for digits 0..3, and the 16 digit-4 trits
-// of a lane in a fifth operand.  The activation operand is permuted to match (a 4 x 4 byte
-// transpose of four 16-code slabs), once per wave and block, shared by the wave's four column
-// tiles.  Pad slabs (k >= K) hold zero trits, so whatever activation codes they meet add 0.
+//   - a lane loads the 16 packed bytes (one 16-byte load) that form its part of the MFMA B
+//     operands for one 320-weight block: row n, bytes 16g..16g+15 of the row's 64-byte block
+//     (g = lane/16);
+//   - all five trits of a byte come from one 8-byte LDS lookup: a table of the 256 byte
+//     values, entry = [t0 t1 t2 t3 | t4 0 0 0] as int8, replicated 32 times (lanes l and l+32
+//     share a copy; an 8-byte read is served 32 lanes at a time, so lookups never conflict);
+//     the lookup address 256*byte + 8*(lane%32) is built by one v_perm_b32.
+// Two table entries are one 16-slot B operand, so an MFMA covers two packed bytes (ten trits
+// and six zero slots): eight MFMAs per 16-row tile and block.  The MFMA only needs A and B to
+// agree on what each of the 64 k-slots holds; the activation operand is assembled to match
+// (a 4 x 4 byte transpose of four 16-code runs plus the fifth digit's codes, shifted into
+// place), once per wave and block, shared by the wave's four column tiles.  The zero slots
+// meet arbitrary activation codes and add 0; so do pad slabs (k >= K), whose trits are 0.
 #include "common.h"
 
 namespace bitnet {
@@ -34,27 +35,6 @@ constexpr int WG_ROWS = DT / 64 * WAVE_ROWS;
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// 3 q in one v_lshl_add_u32 (left to itself the compiler folds w - 3 q into a 64-bit
-// multiply-add, a slow instruction here)
-__device__ __forceinline__ uint32_t times3(uint32_t q)
-{
-    uint32_t r;
-    asm("v_lshl_add_u32 %0, %1, 1, %1" : "=v"(r) : "v"(q));
-    return r;
-}
-
-// trit of the least significant base-3 digit (byte mod 3) of four bytes, as int8
-__device__ __forceinline__ uint32_t trit4(uint32_t w)
-{
-    const uint32_t e = w & 0x00FF00FFu;
-    const uint32_t o = perm(0u, w, 0x0C030C01u);
-    const uint32_t te = __umul24(e, 85u) + 0x00550055u;
-    const uint32_t to = __umul24(o, 85u) + 0x00550055u;
-    const uint32_t q = perm(to, te, 0x07030501u);       // floor(byte / 3), four bytes
-    const uint32_t d = w - times3(q);                    // byte mod 3
-    return perm(0u, 0x000100FFu, d);                     // {0,1,2} -> {-1,0,+1}
 }
 
 // 4 x 4 byte transpose: out[i] = [r0.b_i, r1.b_i, r2.b_i, r3.b_i]
@@ -94,20 +74,22 @@ struct StreamPos {
 template <int BITS, bool DEQ>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
-    __shared__ uint32_t lut[256 * 64];
+    __shared__ __align__(16) uint32_t lut[256 * 64];   // 256 values x 32 copies x 8 bytes
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
     __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < 256 * 64; i += DT) {
-        const int v = i >> 6;
-        uint32_t e = 0;
+    for (int i = tid; i < 256 * 32; i += DT) {
+        const int v = i >> 5;
+        uint32_t lo = 0, hi = 0;
         if (v < 243) {
-            const int d0 = v / 81, d1 = v / 27 % 3, d2 = v / 9 % 3, d3 = v / 3 % 3;
-            e = (uint32_t)(uint8_t)(d0 - 1) | (uint32_t)(uint8_t)(d1 - 1) << 8 |
-                (uint32_t)(uint8_t)(d2 - 1) << 16 | (uint32_t)(uint8_t)(d3 - 1) << 24;
+            const int d0 = v / 81, d1 = v / 27 % 3, d2 = v / 9 % 3, d3 = v / 3 % 3, d4 = v % 3;
+            lo = (uint32_t)(uint8_t)(d0 - 1) | (uint32_t)(uint8_t)(d1 - 1) << 8 |
+                 (uint32_t)(uint8_t)(d2 - 1) << 16 | (uint32_t)(uint8_t)(d3 - 1) << 24;
+            hi = (uint32_t)(uint8_t)(d4 - 1);
         }
-        lut[i] = e;
+        lut[2 * i] = lo;
+        lut[2 * i + 1] = hi;
     }
 
     const int K = a.K, N = a.N, M = a.M;
@@ -119,7 +101,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     const int my_items = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int total = my_items * nblk;
     if (total == 0) return;
-    const uint32_t laneoff = 4u * (uint32_t)lane;
+    const uint32_t laneoff = 8u * (uint32_t)(lane & 31);
     const int g = lane >> 4;
 
     auto start = [&](StreamPos& p, int item) {
@@ -198,53 +180,56 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         if (DEQ && tid == 16) sbuf[buf][16] = x.ws;
     };
 
-    auto lookup = [&](uint32_t w, uint32_t sel) -> int {
-        const uint32_t addr = perm(w, laneoff, sel);    // 256 * byte + 4 * lane
-        return (int)*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lut) + addr);
+    // Entry of byte i of w: [t0 t1 t2 t3] and [t4 0 0 0].
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    auto lookup = [&](uint32_t w, uint32_t sel) -> u2 {
+        const uint32_t addr = perm(w, laneoff, sel);    // 256 * byte + 8 * (lane % 32)
+        return *reinterpret_cast<const u2*>(reinterpret_cast<const uint8_t*>(lut) + addr);
     };
-    auto lookups = [&](const u4& w, v4i (&b)[4]) {
+    // B operand j of a column tile = the entries of the lane's bytes 2j and 2j + 1.
+    auto lookups = [&](const u4& w, v4i (&b)[8]) {
 #pragma unroll
-        for (int u = 0; u < 4; u++)
-            b[u] = v4i{lookup(w[u], 0x0C0C0400u), lookup(w[u], 0x0C0C0500u),
-                       lookup(w[u], 0x0C0C0600u), lookup(w[u], 0x0C0C0700u)};
+        for (int u = 0; u < 4; u++) {
+            const u2 e0 = lookup(w[u], 0x0C0C0400u), e1 = lookup(w[u], 0x0C0C0500u);
+            const u2 e2 = lookup(w[u], 0x0C0C0600u), e3 = lookup(w[u], 0x0C0C0700u);
+            b[2 * u] = v4i{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
+            b[2 * u + 1] = v4i{(int)e2[0], (int)e2[1], (int)e3[0], (int)e3[1]};
+        }
     };
 
     v4i acc[4];
 #pragma unroll
     for (int f = 0; f < 4; f++) acc[f] = v4i{0, 0, 0, 0};
 
-    // One block of one item: table lookups go out two column tiles at a time, ahead of the
-    // MFMAs that consume them.
+    // One block of one item.  The A operand j matching B operand j: for the lane's bytes
+    // p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the codes of digits 0..3 (k = b + 64 i,
+    // b = 16 g + p) and slot 8h + 4 the code of digit 4; slots 8h+5..8h+7 meet zero trits.
     auto compute = [&](const u4 (&w)[4], int buf) {
-        v4i b0[4], b1[4];
+        v4i b0[8], b1[8];
         lookups(w[0], b0);
-        lookups(w[1], b1);
         const uint8_t* ar = abuf[buf] + (lane & 15) * ASTRIDE + 16 * g;
         u4 d[5];
 #pragma unroll
-        for (int j = 0; j < 5; j++) d[j] = *reinterpret_cast<const u4*>(ar + 64 * j);
-        v4i a1[4];
+        for (int i = 0; i < 5; i++) d[i] = *reinterpret_cast<const u4*>(ar + 64 * i);
+        v4i A[8];
 #pragma unroll
-        for (int u = 0; u < 4; u++) a1[u] = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);
-        const v4i a5 = v4i{(int)d[4][0], (int)d[4][1], (int)d[4][2], (int)d[4][3]};
-        v4i t4[4];
+        for (int u = 0; u < 4; u++) {
+            const v4i t = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);   // t[v]: byte 4u + v
+            const uint32_t e = d[4][u];
+            A[2 * u] = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
+            A[2 * u + 1] = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
+        }
+        lookups(w[1], b1);
 #pragma unroll
-        for (int f = 0; f < 4; f++)
-            t4[f] = v4i{(int)trit4(w[f][0]), (int)trit4(w[f][1]), (int)trit4(w[f][2]), (int)trit4(w[f][3])};
-#pragma unroll
-        for (int u = 0; u < 4; u++) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b0[u], acc[0], 0, 0, 0);
+        for (int j = 0; j < 8; j++) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[0], 0, 0, 0);
         lookups(w[2], b0);
 #pragma unroll
-        for (int u = 0; u < 4; u++) acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b1[u], acc[1], 0, 0, 0);
+        for (int j = 0; j < 8; j++) acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[1], 0, 0, 0);
         lookups(w[3], b1);
 #pragma unroll
-        for (int f = 0; f < 2; f++) acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a5, t4[f], acc[f], 0, 0, 0);
+        for (int j = 0; j < 8; j++) acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[2], 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 4; u++) acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b0[u], acc[2], 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 4; u++) acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b1[u], acc[3], 0, 0, 0);
-#pragma unroll
-        for (int f = 2; f < 4; f++) acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a5, t4[f], acc[f], 0, 0, 0);
+        for (int j = 0; j < 8; j++) acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[3], 0, 0, 0);
     };
 
     // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
