@@ -46,6 +46,22 @@ __device__ __forceinline__ v4i transpose4(uint32_t r0, uint32_t r1, uint32_t r2,
                (int)perm(p23h, p01h, 0x05040100u), (int)perm(p23h, p01h, 0x07060302u)};
 }
 
+// The per-layer pointer and scale arrays are never written while a kernel runs; reading them
+// through the constant address space makes them scalar loads (a plain load next to the
+// output stores would be a vector load, and a vector-held buffer address needs a loop).
+typedef const __attribute__((address_space(4))) uint64_t* const_u64_ptr;
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+
+__device__ __forceinline__ const uint8_t* layer_ptr(const uint8_t* const* ptrs, const uint8_t* p0, int l)
+{
+    return ptrs ? (const uint8_t*)((const_u64_ptr)(const void*)ptrs)[l] : p0;
+}
+
+__device__ __forceinline__ float layer_scale(const float* scales, float s0, int l)
+{
+    return scales ? ((const_f32_ptr)(const void*)scales)[l] : s0;
+}
+
 __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
 {
     return ((n ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
@@ -122,7 +138,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int f = 0; f < 4; f++) w_off[f] = (uint32_t)(wave * 4 + f) * tile_bytes + 16u * lane;
     auto load_w = [&](u4 (&dst)[4], const StreamPos& p) {
-        const uint8_t* W = a.wptrs ? a.wptrs[p.l] : a.w0;
+        const uint8_t* W = layer_ptr(a.wptrs, a.w0, p.l);
         const int g0 = p.c * (WG_ROWS / 16);
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(W + (int64_t)g0 * tile_bytes), 0, (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
@@ -136,28 +152,31 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     constexpr int ACH = BITS == 8 ? 20 : 10;            // 16-byte chunks per row and block
     const int q0 = tid, q1 = tid + DT;                  // this thread's chunks (q1 only if < 16*ACH)
     const bool has_q0 = q0 < 16 * ACH, has_q1 = q1 < 16 * ACH;
-    const uint32_t aoff0 = (uint32_t)(q0 / ACH) * (uint32_t)crow + 16u * (q0 % ACH);
-    const uint32_t aoff1 = (uint32_t)(q1 / ACH) * (uint32_t)crow + 16u * (q1 % ACH);
+    const uint32_t c0 = 16u * (q0 % ACH), c1 = 16u * (q1 % ACH);   // chunk offsets in a block
     struct ASlot {
         u4 v0, v1;       // this thread's one or two 16-byte chunks of codes
         float s;         // threads 0..15: activation scale of row tid
         float ws;        // weight scale of the layer (uniform)
     };
     // Branch-free loads: a thread without a chunk reads at an offset past the buffer range,
-    // which returns zeros.
+    // which returns zeros.  A chunk past the end of the row (a pad slab, whose trits are 0)
+    // reads the row's last 16 bytes instead, so no load leaves the row.
     const uint32_t kOut = 0x7FFFFFF0u;
-    const uint32_t aoff0x = has_q0 ? aoff0 : kOut, aoff1x = has_q1 ? aoff1 : kOut;
+    const uint32_t rb0 = has_q0 ? (uint32_t)(q0 / ACH) * (uint32_t)crow : kOut;
+    const uint32_t rb1 = has_q1 ? (uint32_t)(q1 / ACH) * (uint32_t)crow : kOut;
+    const uint32_t clast = (uint32_t)crow - 16u;
     auto load_a = [&](ASlot& dst, const StreamPos& p) {
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (int64_t)p.l * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
-        const int kb = (BITS == 8 ? 320 : 160) * p.B;
-        dst.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff0x, kb, 0);
-        dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)aoff1x, kb, 0);
+        const uint32_t kb = (BITS == 8 ? 320u : 160u) * (uint32_t)p.B;
+        const uint32_t o0 = rb0 + min(kb + c0, clast), o1 = rb1 + min(kb + c1, clast);
+        dst.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o0, 0, 0);
+        dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o1, 0, 0);
         if constexpr (DEQ) {
             const auto ss = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
             dst.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * (tid & 15), 0, 0));
-            dst.ws = a.wscales ? a.wscales[p.l] : a.wscale0;
+            dst.ws = layer_scale(a.wscales, a.wscale0, p.l);
         }
     };
     auto stage_a = [&](int buf, const ASlot& x) {
@@ -204,13 +223,17 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // One block of one item.  The A operand j matching B operand j: for the lane's bytes
     // p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the codes of digits 0..3 (k = b + 64 i,
     // b = 16 g + p) and slot 8h + 4 the code of digit 4; slots 8h+5..8h+7 meet zero trits.
-    auto compute = [&](const u4 (&w)[4], int buf) {
-        v4i b0[8], b1[8];
-        lookups(w[0], b0);
+    // The lookups for column tile 0 (b0) were issued at the end of the previous step; the
+    // lookups for tile f + 1 go out before the MFMAs of tile f (scheduling barriers keep the
+    // compiler from sinking them next to their use).
+    auto compute = [&](const u4 (&w)[4], int buf, v4i (&b0)[8]) {
+        v4i b1[8];
         const uint8_t* ar = abuf[buf] + (lane & 15) * ASTRIDE + 16 * g;
         u4 d[5];
 #pragma unroll
         for (int i = 0; i < 5; i++) d[i] = *reinterpret_cast<const u4*>(ar + 64 * i);
+        lookups(w[1], b1);
+        __builtin_amdgcn_sched_barrier(0);
         v4i A[8];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -219,15 +242,19 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
             A[2 * u] = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
             A[2 * u + 1] = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
         }
-        lookups(w[1], b1);
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         lookups(w[2], b0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         lookups(w[3], b1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[3], 0, 0, 0);
     };
@@ -237,23 +264,26 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     auto finish = [&](const StreamPos& p, int buf) {
         const float wsc = DEQ ? sbuf[buf][16] : 0.0f;
         const int nbase = p.c * WG_ROWS + wave * WAVE_ROWS + (lane & 15);
-        const int64_t obase = (int64_t)p.l * M * N;
+        void* obase = DEQ ? (void*)(a.out + (int64_t)p.l * M * N) : (void*)(a.acc + (int64_t)p.l * M * N);
+        const auto os = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 4 * M * N, 0x00020000);
+        // Buffer stores: an element outside the M x N output gets an offset past the buffer
+        // range and is dropped, so the stores need no branches.
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int mo = 4 * g + r;
             const float sx = DEQ ? sbuf[buf][mo] : 0.0f;
-            if (mo < M) {
 #pragma unroll
-                for (int f = 0; f < 4; f++) {
-                    const int n = nbase + 16 * f;
-                    if (n < N) {
-                        const uint32_t o = (uint32_t)mo * (uint32_t)N + (uint32_t)n;
-                        if constexpr (DEQ)
-                            a.out[obase + o] = ((float)acc[f][r] * sx) * wsc;
-                        else
-                            a.acc[obase + o] = acc[f][r];
-                    }
-                }
+            for (int f = 0; f < 4; f++) {
+                const int n = nbase + 16 * f;
+                uint32_t o = 4u * ((uint32_t)mo * (uint32_t)N + (uint32_t)n);
+                o = mo < M ? o : 0x80000000u;
+                o = n < N ? o : 0x80000000u;
+                uint32_t v;
+                if constexpr (DEQ)
+                    v = __builtin_bit_cast(uint32_t, ((float)acc[f][r] * sx) * wsc);
+                else
+                    v = (uint32_t)acc[f][r];
+                __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, 0);
             }
         }
 #pragma unroll
@@ -282,27 +312,34 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     load_a(x2, pa);                                 // step 2
     load_w(w2, pw);
     __syncthreads();                                // table and step 0 activations in LDS
+    v4i bpre[8];                                    // lookups of the next step's tile 0
+    lookups(w0[0], bpre);
 
-    // Step t: loads for step t + 3, MFMAs of step t, staging of step t + 1.
-    auto step = [&](const u4 (&w)[4], u4 (&wpre)[4], const ASlot& xnext, ASlot& xpre, int t) {
+    // Step t: loads for step t + 3, MFMAs of step t, tile-0 lookups of step t + 1, staging of
+    // step t + 1.
+    auto step = [&](const u4 (&w)[4], const u4 (&wn)[4], u4 (&wpre)[4], const ASlot& xnext,
+                    ASlot& xpre, int t) {
         if (t + 3 < total) { advance(pa); advance(pw); }
         load_a(xpre, pa);
         load_w(wpre, pw);
-        compute(w, t & 1);
+        compute(w, t & 1, bpre);
+        __builtin_amdgcn_sched_barrier(0);
+        lookups(wn[0], bpre);
         stage_a((t + 1) & 1, xnext);
         if (pc.B == nblk - 1) finish(pc, t & 1);
         advance(pc);
         __syncthreads();
     };
-    for (int t = 0; t < total; t += 4) {
-        step(w0, w3, x1, x3, t);
-        if (t + 1 >= total) break;
-        step(w1, w0, x2, x0, t + 1);
-        if (t + 2 >= total) break;
-        step(w2, w1, x3, x1, t + 2);
-        if (t + 3 >= total) break;
-        step(w3, w2, x0, x2, t + 3);
+    int t = 0;
+    for (; t + 4 <= total; t += 4) {
+        step(w0, w1, w3, x1, x3, t);
+        step(w1, w2, w0, x2, x0, t + 1);
+        step(w2, w3, w1, x3, x1, t + 2);
+        step(w3, w0, w2, x0, x2, t + 3);
     }
+    if (t < total) step(w0, w1, w3, x1, x3, t);
+    if (t + 1 < total) step(w1, w2, w0, x2, x0, t + 1);
+    if (t + 2 < total) step(w2, w3, w1, x3, x1, t + 2);
 }
 
 int device_cus()
@@ -330,7 +367,7 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
     // stay below 2 GiB.
     const int64_t packed = (int64_t)((N + 15) / 16) * 16 * 64 * ((K + 319) / 320);
     if (packed >= ((int64_t)1 << 31) || (int64_t)M * K >= ((int64_t)1 << 31) ||
-        (int64_t)M * N >= ((int64_t)1 << 32))
+        4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N};
     const int items = L * ((N + WG_ROWS - 1) / WG_ROWS);
