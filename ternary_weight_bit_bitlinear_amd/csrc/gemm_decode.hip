@@ -79,12 +79,22 @@ struct DecodeArgs {
     int L, M, K, N;
 };
 
+// Cache policy of the weight loads and output stores: non-temporal.  Each weight byte and each
+// output is touched once, so keeping them in the caches only evicts the activation codes,
+// which every 256-row chunk of a layer reads again.
+constexpr int kNonTemporal = 2;
+
 constexpr int ASTRIDE = 336;     // LDS bytes per staged activation row: 320 codes + 16 (banks)
 
 // Position in a workgroup's stream of (item, block) steps.  An item is (layer l, chunk c of
-// 256 weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...
+// 256 weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...  The
+// layer's weight pointer and weight scale are fetched once per item, when the position
+// enters it: a scalar load inside every step would make every step wait for it, and that
+// wait also drains all outstanding LDS reads.
 struct StreamPos {
     int item, B, l, c;
+    const uint8_t* W;
+    float ws;
 };
 
 template <int BITS, bool DEQ>
@@ -125,6 +135,11 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         p.B = 0;
         p.l = item / nchunk;
         p.c = item - p.l * nchunk;
+        // Past the last item the position is never used for data that is kept; clamp the
+        // layer so the pointer and scale reads stay inside their arrays.
+        const int lc = p.l < a.L ? p.l : a.L - 1;
+        p.W = layer_ptr(a.wptrs, a.w0, lc);
+        p.ws = DEQ ? layer_scale(a.wscales, a.wscale0, lc) : 0.0f;
     };
     auto advance = [&](StreamPos& p) {
         if (++p.B == nblk) start(p, p.item + (int)gridDim.x);
@@ -138,12 +153,13 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int f = 0; f < 4; f++) w_off[f] = (uint32_t)(wave * 4 + f) * tile_bytes + 16u * lane;
     auto load_w = [&](u4 (&dst)[4], const StreamPos& p) {
-        const uint8_t* W = layer_ptr(a.wptrs, a.w0, p.l);
+        const uint8_t* W = p.W;
         const int g0 = p.c * (WG_ROWS / 16);
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(W + (int64_t)g0 * tile_bytes), 0, (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
 #pragma unroll
-        for (int f = 0; f < 4; f++) dst[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)w_off[f], 1024 * p.B, 0);
+        for (int f = 0; f < 4; f++)
+            dst[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)w_off[f], 1024 * p.B, kNonTemporal);
     };
 
     // ---- activations: the workgroup stages the 16 rows x 320 codes of a block in LDS with
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
             const auto ss = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
             dst.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * (tid & 15), 0, 0));
-            dst.ws = layer_scale(a.wscales, a.wscale0, p.l);
+            dst.ws = p.ws;
         }
     };
     auto stage_a = [&](int buf, const ASlot& x) {
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
                     v = __builtin_bit_cast(uint32_t, ((float)acc[f][r] * sx) * wsc);
                 else
                     v = (uint32_t)acc[f][r];
-                __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, kNonTemporal);
             }
         }
 #pragma unroll
