@@ -20,6 +20,9 @@
 // (a 4 x 4 byte transpose of four 16-code runs plus the fifth digit's codes, shifted into
 // place), once per wave and block, shared by the wave's four column tiles.  The zero slots
 // meet arbitrary activation codes and add 0; so do pad slabs (k >= K), whose trits are 0.
+// MFMAs go operand by operand, each preceded by the two lookups of the operand six places
+// ahead, so a wave keeps twelve lookups in flight without exceeding what its LDS counter
+// tracks exactly.
 #include "common.h"
 
 namespace bitnet {
@@ -28,8 +31,9 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
-constexpr int DT = 256;        // threads per workgroup: four waves
-constexpr int WAVE_ROWS = 64;  // weight rows per wave: four 16-row MFMA tiles
+constexpr int DT = 256;             // threads per workgroup: four waves
+constexpr int TPW = 4;              // 16-row MFMA column tiles per wave
+constexpr int WAVE_ROWS = 16 * TPW; // weight rows per wave
 constexpr int WG_ROWS = DT / 64 * WAVE_ROWS;
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -149,16 +153,16 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // tile's 16-byte pieces are in lane order, so lane l reads piece l.  Buffer loads: rows
     // past the last 16-row group read as zero (their outputs are not stored).
     const uint32_t tile_bytes = 1024u * (uint32_t)nblk;         // one 16-row group
-    uint32_t w_off[4];
+    uint32_t w_off[TPW];
 #pragma unroll
-    for (int f = 0; f < 4; f++) w_off[f] = (uint32_t)(wave * 4 + f) * tile_bytes + 16u * lane;
-    auto load_w = [&](u4 (&dst)[4], const StreamPos& p) {
+    for (int f = 0; f < TPW; f++) w_off[f] = (uint32_t)(wave * TPW + f) * tile_bytes + 16u * lane;
+    auto load_w = [&](u4 (&dst)[TPW], const StreamPos& p) {
         const uint8_t* W = p.W;
         const int g0 = p.c * (WG_ROWS / 16);
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(W + (int64_t)g0 * tile_bytes), 0, (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
 #pragma unroll
-        for (int f = 0; f < 4; f++)
+        for (int f = 0; f < TPW; f++)
             dst[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)w_off[f], 1024 * p.B, kNonTemporal);
     };
 
@@ -167,7 +171,8 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // activation scales of the item.
     constexpr int ACH = BITS == 8 ? 20 : 10;            // 16-byte chunks per row and block
     const int q0 = tid, q1 = tid + DT;                  // this thread's chunks (q1 only if < 16*ACH)
-    const bool has_q0 = q0 < 16 * ACH, has_q1 = q1 < 16 * ACH;
+    constexpr bool TWO = DT < 16 * ACH;                 // some threads stage two chunks
+    const bool has_q0 = q0 < 16 * ACH, has_q1 = TWO && q1 < 16 * ACH;
     const uint32_t c0 = 16u * (q0 % ACH), c1 = 16u * (q1 % ACH);   // chunk offsets in a block
     struct ASlot {
         u4 v0, v1;       // this thread's one or two 16-byte chunks of codes
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         const uint32_t kb = (BITS == 8 ? 320u : 160u) * (uint32_t)p.B;
         const uint32_t o0 = rb0 + min(kb + c0, clast), o1 = rb1 + min(kb + c1, clast);
         dst.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o0, 0, 0);
-        dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o1, 0, 0);
+        if constexpr (TWO) dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o1, 0, 0);
         if constexpr (DEQ) {
             const auto ss = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
             }
         };
         if (has_q0) put(x.v0, q0);
-        if (has_q1) put(x.v1, q1);
+        if (TWO && has_q1) put(x.v1, q1);
         if (DEQ && tid < 16) sbuf[buf][tid] = x.s;
         if (DEQ && tid == 16) sbuf[buf][16] = x.ws;
     };
@@ -221,58 +226,54 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         const uint32_t addr = perm(w, laneoff, sel);    // 256 * byte + 8 * (lane % 32)
         return *reinterpret_cast<const u2*>(reinterpret_cast<const uint8_t*>(lut) + addr);
     };
-    // B operand j of a column tile = the entries of the lane's bytes 2j and 2j + 1.
-    auto lookups = [&](const u4& w, v4i (&b)[8]) {
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const u2 e0 = lookup(w[u], 0x0C0C0400u), e1 = lookup(w[u], 0x0C0C0500u);
-            const u2 e2 = lookup(w[u], 0x0C0C0600u), e3 = lookup(w[u], 0x0C0C0700u);
-            b[2 * u] = v4i{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
-            b[2 * u + 1] = v4i{(int)e2[0], (int)e2[1], (int)e3[0], (int)e3[1]};
-        }
+    // B operand q of a step (q = TPW j + f: operand j of column tile f) = the entries of the
+    // lane's bytes 2j and 2j + 1 of tile f.
+    auto lookup_op = [&](const u4 (&w)[TPW], int q) -> v4i {
+        const int f = q % TPW, j = q / TPW;
+        const uint32_t word = w[f][j >> 1];
+        const uint32_t sh = (uint32_t)(2 * (j & 1)) << 8;
+        const u2 e0 = lookup(word, 0x0C0C0400u | sh), e1 = lookup(word, 0x0C0C0500u | sh);
+        return v4i{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
     };
 
-    v4i acc[4];
+    v4i acc[TPW];
 #pragma unroll
-    for (int f = 0; f < 4; f++) acc[f] = v4i{0, 0, 0, 0};
+    for (int f = 0; f < TPW; f++) acc[f] = v4i{0, 0, 0, 0};
 
-    // One block of one item.  The A operand j matching B operand j: for the lane's bytes
-    // p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the codes of digits 0..3 (k = b + 64 i,
-    // b = 16 g + p) and slot 8h + 4 the code of digit 4; slots 8h+5..8h+7 meet zero trits.
-    // The lookups for column tile 0 (b0) were issued at the end of the previous step; the
-    // lookups for tile f + 1 go out before the MFMAs of tile f (scheduling barriers keep the
-    // compiler from sinking them next to their use).
-    auto compute = [&](const u4 (&w)[4], int buf, v4i (&b0)[8]) {
-        v4i b1[8];
+    // One block of one item: 32 MFMAs (four column tiles x eight operands).  The A operand j
+    // matching B operand j: for the lane's bytes p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the
+    // codes of digits 0..3 (k = b + 64 i, b = 16 g + p) and slot 8h + 4 the code of digit 4;
+    // slots 8h+5..8h+7 meet zero trits.  The lookups run LA operands ahead of the MFMAs, two
+    // per MFMA, so that 2 LA of them are in flight at each MFMA -- fewer than the 15 LDS
+    // operations a wave can count, so each MFMA waits exactly for its own operand.  The first
+    // LA operands of a step are looked up at the end of the previous step (bn).
+    constexpr int LA = 6;
+    constexpr int NQ = 8 * TPW;       // MFMAs per step
+    auto compute = [&](const u4 (&w)[TPW], int buf, v4i (&bn)[LA]) {
         const uint8_t* ar = abuf[buf] + (lane & 15) * ASTRIDE + 16 * g;
         u4 d[5];
 #pragma unroll
         for (int i = 0; i < 5; i++) d[i] = *reinterpret_cast<const u4*>(ar + 64 * i);
-        lookups(w[1], b1);
-        __builtin_amdgcn_sched_barrier(0);
-        v4i A[8];
+        v4i ring[LA + 1];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const v4i t = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);   // t[v]: byte 4u + v
-            const uint32_t e = d[4][u];
-            A[2 * u] = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
-            A[2 * u + 1] = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
+        for (int i = 0; i < LA; i++) ring[i] = bn[i];
+        v4i A0, A1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < NQ; q++) {
+            const int j = q / TPW, f = q % TPW;
+            if (f == 0 && (j & 1) == 0) {
+                // A operands 2u and 2u + 1 (u = j / 2), used by the next 2 TPW MFMAs
+                const int u = j >> 1;
+                const v4i t = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);   // t[v]: byte 4u + v
+                const uint32_t e = d[4][u];
+                A0 = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
+                A1 = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
+            }
+            if (q + LA < NQ) ring[(q + LA) % (LA + 1)] = lookup_op(w, q + LA);
+            acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8((j & 1) ? A1 : A0, ring[q % (LA + 1)], acc[f], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[0], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        lookups(w[2], b0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        lookups(w[3], b1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b0[j], acc[2], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], b1[j], acc[3], 0, 0, 0);
     };
 
     // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
             const int mo = 4 * g + r;
             const float sx = DEQ ? sbuf[buf][mo] : 0.0f;
 #pragma unroll
-            for (int f = 0; f < 4; f++) {
+            for (int f = 0; f < TPW; f++) {
                 const int n = nbase + 16 * f;
                 uint32_t o = 4u * ((uint32_t)mo * (uint32_t)N + (uint32_t)n);
                 o = mo < M ? o : 0x80000000u;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
             }
         }
 #pragma unroll
-        for (int f = 0; f < 4; f++) acc[f] = v4i{0, 0, 0, 0};
+        for (int f = 0; f < TPW; f++) acc[f] = v4i{0, 0, 0, 0};
     };
 
     // Pipeline: weights run three steps ahead (a four-slot register ring); activations are
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     start(pc, blockIdx.x);
     pa = pc;
     pw = pc;
-    u4 w0[4], w1[4], w2[4], w3[4];                  // weight ring
+    u4 w0[TPW], w1[TPW], w2[TPW], w3[TPW];          // weight ring
     ASlot x0, x1, x2, x3;                           // activation ring
     load_a(x0, pa);                                 // step 0
     load_w(w0, pw);
@@ -328,20 +329,22 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     load_a(x2, pa);                                 // step 2
     load_w(w2, pw);
     __syncthreads();                                // table and step 0 activations in LDS
-    v4i bpre[8];                                    // lookups of the next step's tile 0
-    lookups(w0[0], bpre);
+    v4i bn[LA];                                     // the next step's first operands
+#pragma unroll
+    for (int i = 0; i < LA; i++) bn[i] = lookup_op(w0, i);
 
     // Step t: loads for step t + 3, MFMAs of step t, tile-0 lookups of step t + 1, staging of
     // step t + 1.
-    auto step = [&](const u4 (&w)[4], const u4 (&wn)[4], u4 (&wpre)[4], const ASlot& xnext,
+    auto step = [&](const u4 (&w)[TPW], const u4 (&wn)[TPW], u4 (&wpre)[TPW], const ASlot& xnext,
                     ASlot& xpre, int t) {
         if (t + 3 < total) { advance(pa); advance(pw); }
         load_a(xpre, pa);
         load_w(wpre, pw);
-        compute(w, t & 1, bpre);
-        __builtin_amdgcn_sched_barrier(0);
-        lookups(wn[0], bpre);
+        compute(w, t & 1, bn);
         stage_a((t + 1) & 1, xnext);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < LA; i++) bn[i] = lookup_op(wn, i);
         if (pc.B == nblk - 1) finish(pc, t & 1);
         advance(pc);
         __syncthreads();
