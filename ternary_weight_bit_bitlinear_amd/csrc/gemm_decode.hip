@@ -134,11 +134,20 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     const uint32_t laneoff = 8u * (uint32_t)(lane & 31);
     const int g = lane >> 4;
 
+    // Workgroups are dispatched to the eight XCDs round-robin (workgroup b on XCD b % 8), and
+    // each XCD has its own L2.  When the grid and the item count are multiples of eight, the
+    // workgroup's k-th item slot s = b + k * grid is mapped to item (s % 8) * (items / 8) +
+    // s / 8: each XCD then works through a contiguous range of items (whole layers), and a
+    // layer's activation codes are fetched into one L2 instead of eight.  The mapping is a
+    // bijection on the slots either way.
+    const bool xcd_map = items % 8 == 0 && gridDim.x % 8 == 0;
+    const int per_xcd = items / 8;
     auto start = [&](StreamPos& p, int item) {
         p.item = item;
         p.B = 0;
-        p.l = item / nchunk;
-        p.c = item - p.l * nchunk;
+        const int it = xcd_map && item < items ? (item & 7) * per_xcd + (item >> 3) : item;
+        p.l = it / nchunk;
+        p.c = it - p.l * nchunk;
         // Past the last item the position is never used for data that is kept; clamp the
         // layer so the pointer and scale reads stay inside their arrays.
         const int lc = p.l < a.L ? p.l : a.L - 1;
