@@ -49,6 +49,9 @@ def parse_args():
                    help="only run a plain device-to-device copy of --copy-mib MiB five times "
                         "(the reference point for the HBM byte counters)")
     p.add_argument("--copy-mib", type=int, default=1024)
+    p.add_argument("--vendor-int8", action="store_true",
+                   help="only time the vendor library's dense int8 GEMM at the large-M shapes "
+                        "(context for the int8 MFMA roofline)")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="write the HBM-traffic summary from the four counter runs under DIR "
                         "(fetch/, write/, cal_fetch/, cal_write/) to --out")
@@ -279,6 +282,35 @@ def copy_calibration(torch, mib):
     return {"copy_bytes_per_launch": n, "launches": 5}
 
 
+def vendor_int8(torch):
+    """Context for the large-M roofline: the vendor library's dense int8 GEMM (torch._int_mm,
+    int8 x int8 -> int32, hipBLASLt on ROCm) at the shapes of the three large-M workloads, on
+    plain int8 operands.  It has no ternary decoding, no activation stage and no epilogue; it
+    shows what a tuned int8 MFMA kernel reaches on this GPU at these sizes."""
+    out = {}
+    for name, (M, K, N) in (("wo", (4096, 4096, 4096)), ("wdown", (8192, 16384, 4096)),
+                            ("qkv_gate_up", (16384, 4096, 8192))):
+        g = torch.Generator(device="cuda:0").manual_seed(5)
+        a = torch.randint(-8, 8, (M, K), dtype=torch.int8, device="cuda:0", generator=g)
+        b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device="cuda:0", generator=g)
+        bt = b.t()
+        for _ in range(3):
+            c = torch._int_mm(a, bt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            c = torch._int_mm(a, bt)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        out[name] = dict(M=M, K=K, N=N, us=us, tops=2.0 * M * N * K / (us * 1e-6) / 1e12)
+        log(f"[bench] vendor int8 GEMM {name} {M}x{K}x{N}: {us:.1f} us, {out[name]['tops']:.0f} TOP/s")
+        del a, b, bt, c
+    return out
+
+
 def _counter_means(d, kernel_prefix, counter):
     """Mean per dispatch of `counter` over the dispatches of kernels whose name holds
     `kernel_prefix` (values of one dispatch summed over its instances)."""
@@ -469,6 +501,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         print(json.dumps(copy_calibration(torch, args.copy_mib)), flush=True)
+        return
+    if args.vendor_int8:
+        print(json.dumps({"vendor_int8_gemm": vendor_int8(torch)}), flush=True)
         return
 
     result = {}
