@@ -421,6 +421,7 @@ def run_large(torch, tb, si, config, steps, warmup):
     stream = torch.cuda.current_stream()
     lins = []
     xcache = {}
+    qcache = {}
     for lin in wl.linears:
         key = lin.x_kind
         if key not in xcache:
@@ -428,19 +429,26 @@ def run_large(torch, tb, si, config, steps, warmup):
         W = si.weights(config, lin)
         packed, g = tb.bitnet_pack_weights(W)
         del W
-        codes = torch.empty(tb.hbitlinear_codes_bytes(lin.M, lin.K, lin.act_bits), dtype=torch.uint8,
-                            device=dev)
-        scales = torch.empty(lin.M, dtype=torch.float32, device=dev)
+        # Linears that read the same activations with the same mode (Q, K, V; gate, up) share
+        # one activation stage: its codes and scales are the same for all of them.
+        qkey = (key, lin.act_bits, lin.use_hadamard)
+        first = qkey not in qcache
+        if first:
+            qcache[qkey] = (torch.empty(tb.hbitlinear_codes_bytes(lin.M, lin.K, lin.act_bits),
+                                        dtype=torch.uint8, device=dev),
+                            torch.empty(lin.M, dtype=torch.float32, device=dev))
+        codes, scales = qcache[qkey]
         out = torch.empty((lin.M, lin.N), dtype=torch.float32, device=dev)
-        lins.append((lin, xcache[key], torch.from_numpy(packed).to(dev), g, codes, scales, out))
+        lins.append((lin, xcache[key], torch.from_numpy(packed).to(dev), g, codes, scales, out, first))
     n = len(lins)
 
     def step(tq=None, tg=None):
-        for j, (lin, x, pw, g, codes, scales, out) in enumerate(lins):
-            if tq: tq[j].begin(stream)
-            tb.hbitlinear_quantize(x, lin.act_bits, lin.use_hadamard, codes=codes, scales=scales,
-                                   stream=stream)
-            if tq: tq[j].end(stream)
+        for j, (lin, x, pw, g, codes, scales, out, first) in enumerate(lins):
+            if first:
+                if tq: tq[j].begin(stream)
+                tb.hbitlinear_quantize(x, lin.act_bits, lin.use_hadamard, codes=codes, scales=scales,
+                                       stream=stream)
+                if tq: tq[j].end(stream)
             if tg: tg[j].begin(stream)
             tb.hbitlinear_gemm_dequant(codes, scales, lin.M, lin.K, lin.N, lin.act_bits, pw, g,
                                        out=out, stream=stream)
@@ -459,15 +467,18 @@ def run_large(torch, tb, si, config, steps, warmup):
     M = wl.linears[0].M
     ops = sum(2.0 * l.M * l.N * l.K for l in wl.linears)
     gemm_s = sum(t.mean_ms() for t in tg) * 1e-3
-    quant_s = sum(t.mean_ms() for t in tq) * 1e-3
+    quant_s = sum(t.mean_ms() for t, l in zip(tq, lins) if l[-1]) * 1e-3
     per = {}
     for j, (lin, *_rest) in enumerate(lins):
         g_ms = tg[j].mean_ms()
-        q_ms = tq[j].mean_ms()
         qbytes = 4 * lin.M * lin.K + lin.M * lin.K * lin.act_bits // 8 + 4 * lin.M
-        per[lin.name] = dict(gemm_us=1e3 * g_ms, quant_us=1e3 * q_ms,
-                             gemm_tops=2.0 * lin.M * lin.N * lin.K / (g_ms * 1e-3) / 1e12,
-                             quant_gbs=qbytes / (q_ms * 1e-3) / 1e9)
+        per[lin.name] = dict(gemm_us=1e3 * g_ms,
+                             gemm_tops=2.0 * lin.M * lin.N * lin.K / (g_ms * 1e-3) / 1e12)
+        if lins[j][-1]:
+            q_ms = tq[j].mean_ms()
+            per[lin.name].update(quant_us=1e3 * q_ms, quant_gbs=qbytes / (q_ms * 1e-3) / 1e9)
+        else:
+            per[lin.name].update(quant_shared=True)
     res = dict(workload=wl.name, M=M, ms_per_step=1e3 * dt / steps,
                tokens_per_s=M * steps / dt, int_tops=ops * steps / dt / 1e12,
                gemm_int_tops=ops / gemm_s / 1e12,
