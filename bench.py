@@ -57,6 +57,9 @@ def parse_args():
                         "(fetch/, write/, cal_fetch/, cal_write/) to --out")
     p.add_argument("--summarize-trace", metavar="DIR", default=None,
                    help="write the kernel-trace statistics found under DIR to --out")
+    p.add_argument("--summarize-pmc", metavar="DIR", default=None,
+                   help="write the per-dispatch means of all counters recorded for --kernel under "
+                        "DIR (rocprofv3 --pmc output) to --out")
     p.add_argument("--kernel", default="gemm_decode_kernel")
     p.add_argument("--command", default="", help="command line recorded in a summary")
     p.add_argument("--out", default=None)
@@ -367,6 +370,47 @@ def summarize_counters(args):
     print(text, end="")
 
 
+def summarize_pmc(args):
+    """Means per dispatch of every counter a set of rocprofv3 --pmc runs recorded for one
+    kernel, with the MFMA cross-check: each v_mfma_i32_16x16x64_i8 wave instruction is
+    16 * 16 * 64 multiply-adds = 32768 integer operations."""
+    import csv
+    import glob
+    names = set()
+    for f in glob.glob(os.path.join(args.summarize_pmc, "**", "*_counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if args.kernel in r["Kernel_Name"]:
+                    names.add(r["Counter_Name"])
+    if not names:
+        raise SystemExit(f"no counters for {args.kernel} under {args.summarize_pmc}")
+    means = {}
+    for n in sorted(names):
+        v = list(_counter_means(args.summarize_pmc, args.kernel, n).values())
+        means[n] = (sum(v) / len(v), len(v))
+    lines = [f"# rocprofv3 --pmc counters of {args.kernel}, mean per dispatch", "commands:"]
+    lines += ["  " + c for c in args.command.split(" ;; ") if c]
+    lines.append("")
+    for n, (m, k) in means.items():
+        lines.append(f"{n}: {m:.6g}   ({k} dispatches)")
+    if "SQ_INSTS_MFMA" in means:
+        ops = means["SQ_INSTS_MFMA"][0] * 32768.0
+        lines.append(f"int8 operations from SQ_INSTS_MFMA x 32768: {ops:.6g}")
+    if "SQ_INSTS_VALU_MFMA_MOPS_I8" in means:
+        lines.append(f"int8 operations from SQ_INSTS_VALU_MFMA_MOPS_I8 x 512: "
+                     f"{means['SQ_INSTS_VALU_MFMA_MOPS_I8'][0] * 512.0:.6g}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; the MFMA busy cycles over the 1024 SIMDs
+        busy = means["SQ_VALU_MFMA_BUSY_CYCLES"][0] / 1024.0
+        act = means["GRBM_GUI_ACTIVE"][0] / 8.0
+        lines.append(f"MFMA busy cycles per SIMD: {busy:.6g}; active cycles per XCD: {act:.6g}; "
+                     f"busy fraction {busy / act:.3f}")
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text, end="")
+
+
 def summarize_trace(args):
     """The per-kernel statistics table of a rocprofv3 --kernel-trace --stats run, as text."""
     import csv
@@ -501,6 +545,8 @@ def main():
         return summarize_counters(args)
     if args.summarize_trace:
         return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
 
     import numpy as np  # noqa: F401
     import torch
