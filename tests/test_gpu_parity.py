@@ -316,3 +316,48 @@ def test_decode_kernel_gemm_i32(tb, M, bits):
     acc = tb.bitnet_ternary_gemm_i32(dev(cb.reshape(-1)), M, K, N, bits, dev(packed))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(acc.cpu().numpy(), oracle.gemm(q, oracle.unpack(packed, N, K)))
+
+
+# -------------------------------------------------------------------- graph capture ----
+
+@pytest.mark.parametrize("L,M,K,N,bits,had", [(4, 16, 4096, 512, 8, False), (1, 600, 4096, 384, 4, True)])
+def test_forward_graph_replays_match_eager(tb, L, M, K, N, bits, had):
+    """The grouped forward captured once as a HIP graph (torch.cuda.CUDAGraph) and replayed
+    three times, with eager work and a synchronisation between the replays: every replay
+    gives the eager output bit for bit (the library issues kernel launches only, so the
+    captured graph holds no memset or copy nodes)."""
+    say(f"  graph L={L} M={M} K={K} N={N} bits={bits} had={had}")
+    x = si.normal(si.seed_for(9, 0) + M, L * M * K).reshape(L, M, K)
+    packs, gs = [], []
+    for l in range(L):
+        packed, g = tb.bitnet_pack_weights(si.gaussian_weights(9, N, K, layer=l))
+        packs.append(dev(packed))
+        gs.append(g)
+    ptrs = torch.tensor([p.data_ptr() for p in packs], dtype=torch.int64, device="cuda")
+    wsc = torch.tensor(gs, dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    ws = torch.empty(tb.hbitlinear_grouped_workspace_bytes(L, M, K, bits), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((L, M, N), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        tb.hbitlinear_forward_grouped(xd, N, bits, had, ptrs, wsc, out=out, workspace=ws)
+
+    fwd()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        fwd()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager output"
