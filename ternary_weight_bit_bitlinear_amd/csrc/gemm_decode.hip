@@ -32,9 +32,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 constexpr int DT = 256;             // threads per workgroup: four waves
-constexpr int TPW = 4;              // 16-row MFMA column tiles per wave
-constexpr int WAVE_ROWS = 16 * TPW; // weight rows per wave
-constexpr int WG_ROWS = DT / 64 * WAVE_ROWS;
+// Weight rows of a workgroup's item: four waves of TPW 16-row MFMA column tiles each.  TPW = 4
+// when there are enough items to fill the chip; a single layer of 4096 rows would then be only
+// 16 workgroups, so few-item calls use TPW = 1 (64-row items).
+__host__ __device__ constexpr int wg_rows(int tpw) { return DT / 64 * 16 * tpw; }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
@@ -85,13 +86,13 @@ struct DecodeArgs {
 
 // Cache policy of the weight loads and output stores: non-temporal.  Each weight byte and each
 // output is touched once, so keeping them in the caches only evicts the activation codes,
-// which every 256-row chunk of a layer reads again.
+// which every row chunk of a layer reads again.
 constexpr int kNonTemporal = 2;
 
 constexpr int ASTRIDE = 336;     // LDS bytes per staged activation row: 320 codes + 16 (banks)
 
 // Position in a workgroup's stream of (item, block) steps.  An item is (layer l, chunk c of
-// 256 weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...  The
+// wg_rows(TPW) weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...  The
 // layer's weight pointer and weight scale are fetched once per item, when the position
 // enters it: a scalar load inside every step would make every step wait for it, and that
 // wait also drains all outstanding LDS reads.
@@ -101,9 +102,10 @@ struct StreamPos {
     float ws;
 };
 
-template <int BITS, bool DEQ>
+template <int BITS, bool DEQ, int TPW>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
+    constexpr int WAVE_ROWS = 16 * TPW, WG_ROWS = wg_rows(TPW);
     __shared__ __align__(16) uint32_t lut[256 * 64];   // 256 values x 32 copies x 8 bytes
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
     __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
@@ -384,6 +386,13 @@ int device_cus()
     return cached[dev];
 }
 
+template <int BITS, bool DEQ>
+void launch_decode(bool wide, int grid, const DecodeArgs& a, hipStream_t stream)
+{
+    if (wide) hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4>), dim3(grid), dim3(DT), 0, stream, a);
+    else hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1>), dim3(grid), dim3(DT), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
@@ -398,14 +407,17 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N};
-    const int items = L * ((N + WG_ROWS - 1) / WG_ROWS);
-    const int grid = items < 2 * device_cus() ? items : 2 * device_cus();
+    const int cus = device_cus();
+    const int items4 = L * ((N + wg_rows(4) - 1) / wg_rows(4));
+    const bool wide = items4 >= cus;
+    const int items = wide ? items4 : L * ((N + wg_rows(1) - 1) / wg_rows(1));
+    const int grid = items < 2 * cus ? items : 2 * cus;
     if (out_f32 != nullptr) {
-        if (bits == 8) hipLaunchKernelGGL((gemm_decode_kernel<8, true>), dim3(grid), dim3(DT), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_decode_kernel<4, true>), dim3(grid), dim3(DT), 0, stream, a);
+        if (bits == 8) launch_decode<8, true>(wide, grid, a, stream);
+        else launch_decode<4, true>(wide, grid, a, stream);
     } else {
-        if (bits == 8) hipLaunchKernelGGL((gemm_decode_kernel<8, false>), dim3(grid), dim3(DT), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_decode_kernel<4, false>), dim3(grid), dim3(DT), 0, stream, a);
+        if (bits == 8) launch_decode<8, false>(wide, grid, a, stream);
+        else launch_decode<4, false>(wide, grid, a, stream);
     }
     return hipGetLastError();
 }
