@@ -21,6 +21,9 @@ inline int64_t codes_row_bytes(int K, int bits) { return bits == 8 ? (int64_t)K 
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Compute units of the current device, queried once per device (256 if the query fails).
+int device_cus();
+
 // Internal launchers (quant.hip, gemm.hip).  Arguments are validated by the caller.
 hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
                            uint8_t* codes, float* scales, float* xh, hipStream_t stream);

@@ -25,6 +25,8 @@
 // tracks exactly.
 #include "common.h"
 
+#include <atomic>
+
 namespace bitnet {
 namespace {
 
@@ -372,20 +374,6 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     if (t + 2 < total) step(w2, w3, w1, x3, x1, t + 2);
 }
 
-int device_cus()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int BITS, bool DEQ>
 void launch_decode(bool wide, int grid, const DecodeArgs& a, hipStream_t stream)
 {
@@ -394,6 +382,20 @@ void launch_decode(bool wide, int grid, const DecodeArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+int device_cus()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
                               const uint8_t* const* wptrs, const uint8_t* w0,
