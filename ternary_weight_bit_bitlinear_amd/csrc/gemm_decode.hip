@@ -100,7 +100,9 @@ constexpr int ASTRIDE = 336;     // LDS bytes per staged activation row: 320 cod
 // wait also drains all outstanding LDS reads.
 struct StreamPos {
     int item, B, l, c;
-    const uint8_t* W;
+    __amdgpu_buffer_rsrc_t wrs;   // the item's weight tiles
+    __amdgpu_buffer_rsrc_t crs;   // the layer's activation codes
+    __amdgpu_buffer_rsrc_t srs;   // the layer's activation scales
     float ws;
 };
 
@@ -146,6 +148,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // bijection on the slots either way.
     const bool xcd_map = items % 8 == 0 && gridDim.x % 8 == 0;
     const int per_xcd = items / 8;
+    const uint32_t tile_bytes = 1024u * (uint32_t)nblk;         // one 16-row group of weights
     auto start = [&](StreamPos& p, int item) {
         p.item = item;
         p.B = 0;
@@ -155,7 +158,14 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         // Past the last item the position is never used for data that is kept; clamp the
         // layer so the pointer and scale reads stay inside their arrays.
         const int lc = p.l < a.L ? p.l : a.L - 1;
-        p.W = layer_ptr(a.wptrs, a.w0, lc);
+        const int g0 = p.c * (WG_ROWS / 16);
+        p.wrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(layer_ptr(a.wptrs, a.w0, lc) + (int64_t)g0 * tile_bytes), 0,
+            (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
+        p.crs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.codes + (int64_t)lc * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
+        p.srs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(DEQ ? a.scales + (int64_t)lc * M : nullptr), 0, DEQ ? 4 * M : 0, 0x00020000);
         p.ws = DEQ ? layer_scale(a.wscales, a.wscale0, lc) : 0.0f;
     };
     auto advance = [&](StreamPos& p) {
@@ -165,18 +175,13 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     // ---- weights: one 1 KB tile (16 rows x 64 bytes) per MFMA column tile and block; the
     // tile's 16-byte pieces are in lane order, so lane l reads piece l.  Buffer loads: rows
     // past the last 16-row group read as zero (their outputs are not stored).
-    const uint32_t tile_bytes = 1024u * (uint32_t)nblk;         // one 16-row group
     uint32_t w_off[TPW];
 #pragma unroll
     for (int f = 0; f < TPW; f++) w_off[f] = (uint32_t)(wave * TPW + f) * tile_bytes + 16u * lane;
     auto load_w = [&](u4 (&dst)[TPW], const StreamPos& p) {
-        const uint8_t* W = p.W;
-        const int g0 = p.c * (WG_ROWS / 16);
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(W + (int64_t)g0 * tile_bytes), 0, (int)((uint32_t)(groups - g0) * tile_bytes), 0x00020000);
 #pragma unroll
         for (int f = 0; f < TPW; f++)
-            dst[f] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)w_off[f], 1024 * p.B, kNonTemporal);
+            dst[f] = __builtin_amdgcn_raw_buffer_load_b128(p.wrs, (int)w_off[f], 1024 * p.B, kNonTemporal);
     };
 
     // ---- activations: the workgroup stages the 16 rows x 320 codes of a block in LDS with
@@ -200,16 +205,13 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     const uint32_t rb1 = has_q1 ? (uint32_t)(q1 / ACH) * (uint32_t)crow : kOut;
     const uint32_t clast = (uint32_t)crow - 16u;
     auto load_a = [&](ASlot& dst, const StreamPos& p) {
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.codes + (int64_t)p.l * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
+        const auto rs = p.crs;
         const uint32_t kb = (BITS == 8 ? 320u : 160u) * (uint32_t)p.B;
         const uint32_t o0 = rb0 + min(kb + c0, clast), o1 = rb1 + min(kb + c1, clast);
         dst.v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o0, 0, 0);
         if constexpr (TWO) dst.v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o1, 0, 0);
         if constexpr (DEQ) {
-            const auto ss = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(a.scales + (int64_t)p.l * M), 0, 4 * M, 0x00020000);
-            dst.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, 4 * (tid & 15), 0, 0));
+            dst.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(p.srs, 4 * (tid & 15), 0, 0));
             dst.ws = p.ws;
         }
     };
