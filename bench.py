@@ -237,17 +237,26 @@ def run_decode(torch, tb, d, steps, warmup):
                 gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9)
 
 
-def cpu_baseline_decode(si, oracle, d, tb, layers=2):
-    """The oracle forward on `layers` of the decode layers (host only)."""
-    M, K, N = d["M"], d["K"], d["N"]
-    xs = d["x"][:layers].cpu().numpy()
-    packs = [(d["packs"][l % len(d["packs"])][0].cpu().numpy(), d["g"][l]) for l in range(layers)]
+def cpu_baseline_decode(si, oracle, d, tb, min_seconds=10.0, max_seconds=30.0):
+    """The oracle forward over the decode layers (host only), layer after layer, until at
+    least `min_seconds` have passed (or all layers are done); a layer is never cut short, and
+    no new layer starts after `max_seconds`."""
+    M, K, N, L = d["M"], d["K"], d["N"], d["L"]
+    xs = d["x"].cpu().numpy()
+    unique = len(d["packs"])
+    packs = [(p.cpu().numpy(), g) for p, g in d["packs"]]
+    layers = 0
     t0 = time.perf_counter()
-    for l in range(layers):
-        oracle.forward(xs[l], packs[l][0], packs[l][1], N, 8, False)
+    while layers < L:
+        p, g = packs[layers % unique]
+        oracle.forward(xs[layers], p, g, N, 8, False)
+        layers += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el >= max_seconds:
+            break
     dt = time.perf_counter() - t0
     return dict(value=M * layers / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{layers} of the {d['L']} layers at M={M} (unpack + quantise + add/sub "
+                sample=f"{layers} of the {L} layers at M={M} (unpack + quantise + add/sub "
                        f"product + epilogue per layer), {dt:.1f} s")
 
 
@@ -618,7 +627,7 @@ def main():
             "int_tops": r["int_tops"],
             "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gemm_decode_kernel<8,true>", "launch_us": r["gemm_us"],
+                         "kernel": "gemm_decode_kernel<8,true,4>", "launch_us": r["gemm_us"],
                          "algorithmic_bytes_per_launch": r["gemm_bytes"]},
             "quant_kernel_us": r["quant_us"],
             "decode_sequential": sequential,
