@@ -109,14 +109,20 @@ struct StreamPos {
 template <int BITS, bool DEQ, int TPW>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
+    static_assert(DT == 256, "one thread per byte value forms the table");
     constexpr int WAVE_ROWS = 16 * TPW, WG_ROWS = wg_rows(TPW);
     __shared__ __align__(16) uint32_t lut[256 * 64];   // 256 values x 32 copies x 8 bytes
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
     __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < 256 * 32; i += DT) {
-        const int v = i >> 5;
+    {
+        // The table: thread v forms the entry of byte value v once (DT = 256 threads, one per
+        // value), in the second activation buffer, which is free until the first staging;
+        // then the threads fill the 32 replicas with 16-byte stores, consecutive lanes on
+        // consecutive 16-byte chunks (chunk q: value q / 16, replicas 2 (q % 16) and + 1).
+        uint32_t* ent = reinterpret_cast<uint32_t*>(abuf[1]);
+        const int v = tid;
         uint32_t lo = 0, hi = 0;
         if (v < 243) {
             const int d0 = v / 81, d1 = v / 27 % 3, d2 = v / 9 % 3, d3 = v / 3 % 3, d4 = v % 3;
@@ -124,8 +130,14 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
                  (uint32_t)(uint8_t)(d2 - 1) << 16 | (uint32_t)(uint8_t)(d3 - 1) << 24;
             hi = (uint32_t)(uint8_t)(d4 - 1);
         }
-        lut[2 * i] = lo;
-        lut[2 * i + 1] = hi;
+        ent[2 * v] = lo;
+        ent[2 * v + 1] = hi;
+        __syncthreads();
+        for (int q = tid; q < 256 * 16; q += DT) {
+            const uint32_t e0 = ent[2 * (q >> 4)], e1 = ent[2 * (q >> 4) + 1];
+            *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(lut) + 16 * q) = u4{e0, e1, e0, e1};
+        }
+        __syncthreads();
     }
 
     const int K = a.K, N = a.N, M = a.M;
