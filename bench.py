@@ -596,11 +596,18 @@ def main():
             log(f"[bench] decode grouped M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm "
                 f"{rm['gemm_us']:.1f} us ({rm['gemm_gbs']:.0f} GB/s)")
             del dm
-        cpu = None
+        cpu = cpu1 = None
         if not args.no_cpu_baseline and args.only != "headline":
             import oracle
             log("[bench] cpu baseline (oracle)")
             cpu = cpu_baseline_decode(si, oracle, d, tb)
+            # the same oracle on one host thread, as context
+            nthr = oracle.num_threads()
+            oracle.set_num_threads(1)
+            try:
+                cpu1 = cpu_baseline_decode(si, oracle, d, tb, min_seconds=3.0, max_seconds=10.0)
+            finally:
+                oracle.set_num_threads(nthr)
         workload = f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_grouped_L{d['L']}"
         traffic = recorded_traffic("gemm_decode_kernel", f"M{d['M']}_L{d['L']}")
         result = {
@@ -633,6 +640,7 @@ def main():
             "decode_sequential": sequential,
             "decode_other_M": others,
             "cpu_baseline": cpu,
+            "cpu_baseline_1thread": cpu1,
         }
         del d
         torch.cuda.empty_cache()
