@@ -465,26 +465,29 @@ void gemm_tern4_kernel(LargeArgs args)
     };
 
     // Prologue: weights of block 0 (then 1 in flight); codes of slabs 0..3 in LDS; trits of
-    // slabs 0 and 1; operands of slab 0 in registers (A tiles 4..7 still packed).
+    // slabs 0 and 1; operands of slab 0 in registers (A tiles 4..7 still packed).  The codes
+    // and scales are requested together with the first weights, so the prologue waits for
+    // one round trip to memory, not two.
     load_w(wnext, 0);
+    load_a(0, 0);
+    load_a(1, 1);
+    load_a(2, 2);
+    load_a(3, 3);
+    constexpr int NSX = DEQ ? BM / NT : 0;            // scale loads
     if constexpr (DEQ) {
         // s_x of the tile's rows straight into LDS, 64 rows per wave-wide load; rows past M
         // read as zero.
         const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)(args.scales + (int64_t)layer * M), 0, 4 * M, 0x00020000);
 #pragma unroll
-        for (int s = 0; s < BM / NT; s++)
+        for (int s = 0; s < NSX; s++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr)(sxs + NT * s + 64 * wave), 4,
                                                      4u * (uint32_t)(m0 + NT * s + 64 * wave + lane), 0, 0, 0);
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<4 * AJ + NSX>();                         // the two weight loads of block 0
     take_block(1);
-    load_a(0, 0);
-    load_a(1, 1);
-    load_a(2, 2);
-    load_a(3, 3);
     produce(0);
     produce(1);
-    wait_vmcnt<0>();
+    wait_vmcnt<2>();                                    // all but block 1's two weight loads
     block_sync();
     v4i af[8], bf[8];
     ARaw rhi[4];
