@@ -88,6 +88,10 @@ class Timer:
     def mean_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
 
+    def median_ms(self):
+        v = sorted(a.elapsed_time(b) for a, b in self.pairs[: self.i])
+        return v[len(v) // 2] if v else 0.0
+
 
 def canonical_packed_bytes(N, K):
     # five trits per byte with nothing wasted: the algorithmic weight bytes
@@ -185,6 +189,7 @@ def run_decode_grouped(torch, tb, d, steps, warmup):
         step(stream, tq, tg)
     torch.cuda.synchronize()
     gemm_ms = tg.mean_ms()
+    gemm_ms_median = tg.median_ms()
     check()
     # timed pass
     torch.cuda.synchronize()
@@ -197,6 +202,7 @@ def run_decode_grouped(torch, tb, d, steps, warmup):
     bytes_gemm = L * decode_gemm_bytes(M, K, N)
     return dict(seconds=dt, ms_per_step=1e3 * dt / steps, tokens_per_s=M * L * steps / dt,
                 int_tops=2.0 * M * N * K * L * steps / dt / 1e12, gemm_us=1e3 * gemm_ms,
+                gemm_us_median=1e3 * gemm_ms_median,
                 quant_us=1e3 * tq.mean_ms(), gemm_bytes=bytes_gemm,
                 gemm_gbs=bytes_gemm / (gemm_ms * 1e-3) / 1e9)
 
@@ -519,6 +525,15 @@ def run_large(torch, tb, si, config, steps, warmup):
     dt = time.perf_counter() - t0
     M = wl.linears[0].M
     ops = sum(2.0 * l.M * l.N * l.K for l in wl.linears)
+    # HBM bytes of a step at the algorithmic minimum: every activation stage reads x and writes
+    # codes and scales once; every product reads codes, scales and packed weights (canonical
+    # five trits per byte) and writes y.
+    e2e_bytes = 0.0
+    for lin, *_r, first in lins:
+        cb = lin.M * lin.K * lin.act_bits // 8
+        if first:
+            e2e_bytes += 4 * lin.M * lin.K + cb + 4 * lin.M
+        e2e_bytes += cb + 4 * lin.M + canonical_packed_bytes(lin.N, lin.K) + 4 * lin.M * lin.N
     gemm_s = sum(t.mean_ms() for t in tg) * 1e-3
     quant_s = sum(t.mean_ms() for t, l in zip(tq, lins) if l[-1]) * 1e-3
     per = {}
@@ -537,6 +552,8 @@ def run_large(torch, tb, si, config, steps, warmup):
                gemm_int_tops=ops / gemm_s / 1e12,
                gemm_mfma_frac=ops / gemm_s / 1e12 / INT8_PEAK_TOPS,
                end_to_end_mfma_frac=ops * steps / dt / 1e12 / INT8_PEAK_TOPS,
+               end_to_end_roofline_frac=max(e2e_bytes / (HBM_PEAK_GBS * 1e9),
+                                            ops / (INT8_PEAK_TOPS * 1e12)) / (dt / steps),
                quant_share=quant_s / (quant_s + gemm_s), linears=per)
     del lins, xcache
     torch.cuda.empty_cache()
@@ -635,6 +652,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                          "kernel": "gemm_decode_kernel<8,true,4>", "launch_us": r["gemm_us"],
+                         "launch_us_median": r["gemm_us_median"],
                          "algorithmic_bytes_per_launch": r["gemm_bytes"]},
             "quant_kernel_us": r["quant_us"],
             "decode_sequential": sequential,
