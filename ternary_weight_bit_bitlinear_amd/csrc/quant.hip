@@ -28,7 +28,10 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-__host__ __device__ constexpr int threads_for(int L) { return L >= 12 ? (1 << (L - 6)) : 64; }
+// Threads per row: 64 up to K = 2048, then K / 32 (32 elements per thread).  Fewer elements
+// per thread (more waves per row) hide more of the load latency; 16 per thread measured slower
+// (one more LDS exchange), 64 per thread slower at K >= 4096.
+__host__ __device__ constexpr int threads_for(int L) { return L >= 12 ? (1 << (L - 5)) : 64; }
 __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v >> 1); }
 
 // Deposit the low bits of v into the set bits of mask, lowest first.
