@@ -27,7 +27,9 @@
  *     faults surface at the caller's next synchronisation, as for any HIP kernel.
  *   - Supported shapes: 1 <= M, 1 <= N, 64 <= K <= 65536 with K % 64 == 0; with
  *     use_hadamard = 1, K must be a power of two, 256 <= K <= 16384.  act_bits is 4 or 8.
- *     Anything else returns BITNET_ERR_UNSUPPORTED (or BITNET_ERR_SHAPE for sizes <= 0).
+ *     Per layer, the packed weights, the activation codes and the output (4 M N bytes) must
+ *     each stay below 2 GiB.  Anything else returns BITNET_ERR_UNSUPPORTED (or
+ *     BITNET_ERR_SHAPE for sizes <= 0).
  */
 #ifndef BITNET_H
 #define BITNET_H

@@ -20,6 +20,17 @@ int check_shape(int M, int K, int N, int bits, int use_hadamard)
     return BITNET_OK;
 }
 
+// The product kernels address one layer's packed weights, codes and output with 32-bit
+// buffer offsets: each must stay below 2 GiB.
+int check_gemm_limits(int M, int K, int N, int bits)
+{
+    const int64_t packed = (int64_t)1024 * ((N + 15) / 16) * ((K + 319) / 320);
+    const int64_t codes = (int64_t)M * codes_row_bytes(K, bits);
+    const int64_t out = (int64_t)4 * M * N;
+    const int64_t lim = (int64_t)1 << 31;
+    return packed < lim && codes < lim && out < lim ? BITNET_OK : BITNET_ERR_UNSUPPORTED;
+}
+
 int status_of(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_HIP; }
 
 size_t codes_bytes(int M, int K, int bits) { return (size_t)M * (size_t)codes_row_bytes(K, bits); }
@@ -82,6 +93,7 @@ int bitnet_ternary_gemm_i32(const uint8_t* codes, int M, int K, int N, int act_b
 {
     if (codes == nullptr || packed_w == nullptr || acc == nullptr) return BITNET_ERR_NULL;
     int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
     if (rc != BITNET_OK) return rc;
     return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, nullptr, nullptr,
                                  0.0f, nullptr, acc, (hipStream_t)stream));
@@ -94,6 +106,7 @@ int hbitlinear_gemm_dequant(const uint8_t* codes, const float* scales, int M, in
     if (codes == nullptr || scales == nullptr || packed_w == nullptr || out == nullptr)
         return BITNET_ERR_NULL;
     int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
     if (rc != BITNET_OK) return rc;
     return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
                                  w_scale, out, nullptr, (hipStream_t)stream));
@@ -105,6 +118,7 @@ int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int us
 {
     if (x == nullptr || out == nullptr || packed_w == nullptr) return BITNET_ERR_NULL;
     int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
     if (rc != BITNET_OK) return rc;
     if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
         return BITNET_ERR_WORKSPACE;
@@ -126,6 +140,7 @@ int hbitlinear_gemm_dequant_grouped(const uint8_t* codes, const float* scales, i
         return BITNET_ERR_NULL;
     if (L <= 0) return BITNET_ERR_SHAPE;
     int rc = check_shape(M, K, N, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
     if (rc != BITNET_OK) return rc;
     if ((int64_t)L * M > (int64_t)1 << 30 || L > 65535) return BITNET_ERR_UNSUPPORTED;
     return status_of(launch_gemm(codes, L, M, K, N, act_bits, packed_ws, nullptr, scales, w_scales,
@@ -152,6 +167,7 @@ int hbitlinear_forward_grouped(int L, const float* x, int M, int K, int N, int a
         return BITNET_ERR_NULL;
     if (L <= 0) return BITNET_ERR_SHAPE;
     int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
     if (rc != BITNET_OK) return rc;
     if ((int64_t)L * M > (int64_t)1 << 30 || L > 65535) return BITNET_ERR_UNSUPPORTED;
     const int rows = L * M;

@@ -128,6 +128,10 @@ NUL = ctypes.c_void_p(None)
     ((FAKE, 4, 4032, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
     ((FAKE, 4, 128, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
     ((FAKE, 4, 32768, 64, 8, 1, FAKE, FAKE, FAKE, 1 << 30), tb.BITNET_ERR_UNSUPPORTED),
+    # an output of 4 M N >= 2 GiB, a layer's codes >= 2 GiB, packed weights >= 2 GiB
+    ((FAKE, 16384, 4096, 32768, 8, 0, FAKE, FAKE, FAKE, 1 << 30), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 1 << 16, 32768, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 40), tb.BITNET_ERR_UNSUPPORTED),
+    ((FAKE, 1, 65536, 200000, 8, 0, FAKE, FAKE, FAKE, 1 << 20), tb.BITNET_ERR_UNSUPPORTED),
     ((FAKE, 4, 4096, 64, 8, 0, FAKE, FAKE, NUL, 1 << 20), tb.BITNET_ERR_WORKSPACE),
     ((FAKE, 4, 4096, 64, 8, 0, FAKE, FAKE, FAKE, 4 * 4096), tb.BITNET_ERR_WORKSPACE),
 ])
@@ -147,3 +151,8 @@ def test_stage_validation():
     assert L.hbitlinear_gemm_dequant(FAKE, NUL, 4, 256, 8, 4, FAKE, ctypes.c_float(1.0), FAKE,
                                      NUL) == tb.BITNET_ERR_NULL
     assert L.bitnet_pack_weights(NUL, 1, 1, FAKE, FAKE) == tb.BITNET_ERR_NULL
+    # the product stages refuse outputs of 2 GiB or more before launching anything
+    assert L.bitnet_ternary_gemm_i32(FAKE, 16384, 256, 32768, 8, FAKE, FAKE, NUL) == \
+        tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_gemm_dequant(FAKE, FAKE, 16384, 256, 32768, 4, FAKE, ctypes.c_float(1.0),
+                                     FAKE, NUL) == tb.BITNET_ERR_UNSUPPORTED
