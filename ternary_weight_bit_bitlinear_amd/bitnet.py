@@ -75,9 +75,11 @@ def _ptr(t) -> ctypes.c_void_p:
     if t is None:
         return ctypes.c_void_p(None)
     if isinstance(t, np.ndarray):
-        assert t.flags["C_CONTIGUOUS"]
+        if not t.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
         return ctypes.c_void_p(t.ctypes.data)
-    assert t.is_contiguous(), "tensor must be contiguous"
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
 
