@@ -23,9 +23,15 @@
 // MFMAs go operand by operand, each preceded by the two lookups of the operand six places
 // ahead, so a wave keeps twelve lookups in flight without exceeding what its LDS counter
 // tracks exactly.
+//
+// Two kernels share that inner step: a persistent streaming kernel that walks (layer, row
+// chunk) items block by block with the activations staged in LDS, for calls that give every
+// CU work; and a split-K kernel for calls of a few thousand rows, in which the four waves of a
+// workgroup divide one 16-row group's blocks and add their partial tiles at the end.
 #include "common.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace bitnet {
 namespace {
@@ -93,6 +99,89 @@ constexpr int kNonTemporal = 2;
 
 constexpr int ASTRIDE = 336;     // LDS bytes per staged activation row: 320 codes + 16 (banks)
 
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+// Table entry of byte value v (< 256): the five base-3 digits, most significant first, each
+// minus one, as int8 -- lo = digits 0..3, hi = digit 4 -- or zeros for v >= 243, a value no
+// packed byte takes.  floor(x / 3) = (171 x) >> 9 for x < 256 (171 / 512 exceeds 1/3 by
+// less than 1/(3 * 256)); a byte b in 0..2 becomes b - 1 as ((b | 0x80) - 1) ^ 0x80, four
+// bytes at a time without borrows.
+__device__ __forceinline__ void table_entry(uint32_t v, uint32_t& lo, uint32_t& hi)
+{
+    const uint32_t q1 = (171u * v) >> 9, q2 = (171u * q1) >> 9, q3 = (171u * q2) >> 9, q4 = (171u * q3) >> 9;
+    const uint32_t d4 = v - 3u * q1, d3 = q1 - 3u * q2, d2 = q2 - 3u * q3, d1 = q3 - 3u * q4, d0 = q4;
+    const uint32_t packed = d0 | d1 << 8 | d2 << 16 | d3 << 24;
+    lo = v < 243u ? ((packed | 0x80808080u) - 0x01010101u) ^ 0x80808080u : 0u;
+    hi = v < 243u ? (d4 - 1u) & 0xFFu : 0u;
+}
+
+// The lookup table, 256 values x 32 replicas x 8 bytes, filled with 16-byte stores (chunk q:
+// value q / 16, replicas 2 (q % 16) and + 1), consecutive threads on consecutive chunks.
+// Every entry is computed where it is stored, so the stores do not wait on anything.
+__device__ __forceinline__ void build_table(uint32_t* lut, int tid)
+{
+    static_assert(256 * 16 % DT == 0, "chunks per thread");
+#pragma unroll
+    for (int j = 0; j < 256 * 16 / DT; j++) {
+        const int q = tid + DT * j;
+        uint32_t lo, hi;
+        table_entry((uint32_t)(q >> 4), lo, hi);
+        *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(lut) + 16 * q) = u4{lo, hi, lo, hi};
+    }
+    __syncthreads();
+}
+
+// B operand q of a block (q = TPW j + f: operand j of column tile f) = the table entries of the
+// lane's bytes 2j and 2j + 1 of tile f; the lookup address 256 * byte + 8 * (lane % 32)
+// (laneoff = 8 * (lane % 32)) is one byte permute.
+template <int TPW>
+__device__ __forceinline__ v4i lookup_operand(const uint32_t* lut, uint32_t laneoff, const u4 (&w)[TPW], int q)
+{
+    const int f = q % TPW, j = q / TPW;
+    const uint32_t word = w[f][j >> 1];
+    const uint32_t sh = (uint32_t)(2 * (j & 1)) << 8;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(lut);
+    const u2 e0 = *reinterpret_cast<const u2*>(base + perm(word, laneoff, 0x0C0C0400u | sh));
+    const u2 e1 = *reinterpret_cast<const u2*>(base + perm(word, laneoff, 0x0C0C0500u | sh));
+    return v4i{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
+}
+
+// The 8 TPW MFMAs of one 320-weight block for TPW column tiles.  d[i]: the lane's 16 codes of
+// digit slab i, k = 320 B + 64 i + 16 g + (0..15) of row lane & 15.  The A operand j matching B operand j:
+// for the lane's bytes p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the codes of digits 0..3
+// (k = b + 64 i, b = 16 g + p) and slot 8h + 4 the code of digit 4; slots 8h+5..8h+7 meet
+// zero trits.  The lookups run LA operands ahead of the MFMAs, two per MFMA, so that 2 LA of
+// them are in flight at each MFMA -- fewer than the 15 LDS operations a wave can count, so
+// each MFMA waits exactly for its own operand.  bn: the block's first LA operands.
+template <int TPW, int LA>
+__device__ __forceinline__ void block_mfmas(const uint32_t* lut, uint32_t laneoff, const u4 (&d)[5],
+                                            const u4 (&w)[TPW], const v4i (&bn)[LA], v4i (&acc)[TPW])
+{
+    constexpr int NQ = 8 * TPW;
+    v4i ring[LA + 1];
+#pragma unroll
+    for (int i = 0; i < LA; i++) ring[i] = bn[i];
+    v4i A0, A1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+        const int j = q / TPW, f = q % TPW;
+        if (f == 0 && (j & 1) == 0) {
+            // A operands 2u and 2u + 1 (u = j / 2), used by the next 2 TPW MFMAs
+            const int u = j >> 1;
+            const v4i t = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);   // t[v]: byte 4u + v
+            const uint32_t e = d[4][u];
+            A0 = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
+            A1 = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
+        }
+        if (q + LA < NQ) ring[(q + LA) % (LA + 1)] = lookup_operand<TPW>(lut, laneoff, w, q + LA);
+        acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8((j & 1) ? A1 : A0, ring[q % (LA + 1)], acc[f], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+constexpr int kLookahead = 6;
+
 // Position in a workgroup's stream of (item, block) steps.  An item is (layer l, chunk c of
 // wg_rows(TPW) weight rows); the workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...  The
 // layer's weight pointer and weight scale are fetched once per item, when the position
@@ -109,36 +198,13 @@ struct StreamPos {
 template <int BITS, bool DEQ, int TPW>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
-    static_assert(DT == 256, "one thread per byte value forms the table");
     constexpr int WAVE_ROWS = 16 * TPW, WG_ROWS = wg_rows(TPW);
     __shared__ __align__(16) uint32_t lut[256 * 64];   // 256 values x 32 copies x 8 bytes
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
     __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    {
-        // The table: thread v forms the entry of byte value v once (DT = 256 threads, one per
-        // value), in the second activation buffer, which is free until the first staging;
-        // then the threads fill the 32 replicas with 16-byte stores, consecutive lanes on
-        // consecutive 16-byte chunks (chunk q: value q / 16, replicas 2 (q % 16) and + 1).
-        uint32_t* ent = reinterpret_cast<uint32_t*>(abuf[1]);
-        const int v = tid;
-        uint32_t lo = 0, hi = 0;
-        if (v < 243) {
-            const int d0 = v / 81, d1 = v / 27 % 3, d2 = v / 9 % 3, d3 = v / 3 % 3, d4 = v % 3;
-            lo = (uint32_t)(uint8_t)(d0 - 1) | (uint32_t)(uint8_t)(d1 - 1) << 8 |
-                 (uint32_t)(uint8_t)(d2 - 1) << 16 | (uint32_t)(uint8_t)(d3 - 1) << 24;
-            hi = (uint32_t)(uint8_t)(d4 - 1);
-        }
-        ent[2 * v] = lo;
-        ent[2 * v + 1] = hi;
-        __syncthreads();
-        for (int q = tid; q < 256 * 16; q += DT) {
-            const uint32_t e0 = ent[2 * (q >> 4)], e1 = ent[2 * (q >> 4) + 1];
-            *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(lut) + 16 * q) = u4{e0, e1, e0, e1};
-        }
-        __syncthreads();
-    }
+    build_table(lut, tid);
 
     const int K = a.K, N = a.N, M = a.M;
     const int nblk = (K + 319) / 320;
@@ -247,60 +313,21 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
         if (DEQ && tid == 16) sbuf[buf][16] = x.ws;
     };
 
-    // Entry of byte i of w: [t0 t1 t2 t3] and [t4 0 0 0].
-    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-    auto lookup = [&](uint32_t w, uint32_t sel) -> u2 {
-        const uint32_t addr = perm(w, laneoff, sel);    // 256 * byte + 8 * (lane % 32)
-        return *reinterpret_cast<const u2*>(reinterpret_cast<const uint8_t*>(lut) + addr);
-    };
-    // B operand q of a step (q = TPW j + f: operand j of column tile f) = the entries of the
-    // lane's bytes 2j and 2j + 1 of tile f.
-    auto lookup_op = [&](const u4 (&w)[TPW], int q) -> v4i {
-        const int f = q % TPW, j = q / TPW;
-        const uint32_t word = w[f][j >> 1];
-        const uint32_t sh = (uint32_t)(2 * (j & 1)) << 8;
-        const u2 e0 = lookup(word, 0x0C0C0400u | sh), e1 = lookup(word, 0x0C0C0500u | sh);
-        return v4i{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
-    };
+    auto lookup_op = [&](const u4 (&w)[TPW], int q) -> v4i { return lookup_operand<TPW>(lut, laneoff, w, q); };
 
     v4i acc[TPW];
 #pragma unroll
     for (int f = 0; f < TPW; f++) acc[f] = v4i{0, 0, 0, 0};
 
-    // One block of one item: 32 MFMAs (four column tiles x eight operands).  The A operand j
-    // matching B operand j: for the lane's bytes p = 2j + h (h = 0, 1), slots 8h..8h+3 hold the
-    // codes of digits 0..3 (k = b + 64 i, b = 16 g + p) and slot 8h + 4 the code of digit 4;
-    // slots 8h+5..8h+7 meet zero trits.  The lookups run LA operands ahead of the MFMAs, two
-    // per MFMA, so that 2 LA of them are in flight at each MFMA -- fewer than the 15 LDS
-    // operations a wave can count, so each MFMA waits exactly for its own operand.  The first
-    // LA operands of a step are looked up at the end of the previous step (bn).
-    constexpr int LA = 6;
-    constexpr int NQ = 8 * TPW;       // MFMAs per step
+    // One block of one item: 8 TPW MFMAs; the first kLookahead operands of a step are looked
+    // up at the end of the previous step (bn).
+    constexpr int LA = kLookahead;
     auto compute = [&](const u4 (&w)[TPW], int buf, v4i (&bn)[LA]) {
         const uint8_t* ar = abuf[buf] + (lane & 15) * ASTRIDE + 16 * g;
         u4 d[5];
 #pragma unroll
         for (int i = 0; i < 5; i++) d[i] = *reinterpret_cast<const u4*>(ar + 64 * i);
-        v4i ring[LA + 1];
-#pragma unroll
-        for (int i = 0; i < LA; i++) ring[i] = bn[i];
-        v4i A0, A1;
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < NQ; q++) {
-            const int j = q / TPW, f = q % TPW;
-            if (f == 0 && (j & 1) == 0) {
-                // A operands 2u and 2u + 1 (u = j / 2), used by the next 2 TPW MFMAs
-                const int u = j >> 1;
-                const v4i t = transpose4(d[0][u], d[1][u], d[2][u], d[3][u]);   // t[v]: byte 4u + v
-                const uint32_t e = d[4][u];
-                A0 = v4i{t[0], (int)e, t[1], (int)(e >> 8)};
-                A1 = v4i{t[2], (int)(e >> 16), t[3], (int)(e >> 24)};
-            }
-            if (q + LA < NQ) ring[(q + LA) % (LA + 1)] = lookup_op(w, q + LA);
-            acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8((j & 1) ? A1 : A0, ring[q % (LA + 1)], acc[f], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        block_mfmas<TPW, LA>(lut, laneoff, d, w, bn, acc);
     };
 
     // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
@@ -388,11 +415,147 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     if (t + 2 < total) step(w2, w3, w1, x3, x1, t + 2);
 }
 
+// Few-item calls (one layer of a few thousand rows): a workgroup per 16-row weight group, the
+// group's K blocks split over the four waves (wave w takes blocks w, w + 4, ...), so that a
+// 4096-row layer is 256 workgroups with a few blocks per wave instead of 64 workgroups that
+// each walk all the blocks.  A wave reads its activation operands straight from memory (the
+// layer's codes stay in the L2): the lane's 16 codes of each digit slab are one load.  Each
+// wave prefetches four blocks; the four partial int32 tiles are added in LDS (integer sums,
+// exact in any order) and the sum goes through the same epilogue as the streaming kernel.
 template <int BITS, bool DEQ>
-void launch_decode(bool wide, int grid, const DecodeArgs& a, hipStream_t stream)
+__global__ __launch_bounds__(DT, 2) void gemm_decode_splitk_kernel(DecodeArgs a)
 {
-    if (wide) hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4>), dim3(grid), dim3(DT), 0, stream, a);
-    else hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1>), dim3(grid), dim3(DT), 0, stream, a);
+    static_assert(DT == 256, "four waves: one per register of the summed tile");
+    __shared__ __align__(16) uint32_t lut[256 * 64];
+    __shared__ __align__(16) int32_t part[4 * 64 * 4];   // partial tiles: wave, lane, register
+
+    // The wave index is made visibly uniform: the wave's block count then steers scalar
+    // branches and selects instead of per-lane control flow.
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = a.K, N = a.N, M = a.M;
+    const int nblk = (K + 319) / 320;
+    const int crow = BITS == 8 ? K : K / 2;
+    const int groups = (N + 15) / 16;
+    const int l = (int)blockIdx.x / groups, gi = (int)blockIdx.x - l * groups;
+    const uint32_t tile_bytes = 1024u * (uint32_t)nblk;
+    const auto wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(layer_ptr(a.wptrs, a.w0, l) + (int64_t)gi * tile_bytes), 0, (int)tile_bytes, 0x00020000);
+    // Rows past M fall outside the range and read as zero (their outputs are not stored).
+    const auto crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.codes + (int64_t)l * M * crow), 0, (int)((uint32_t)M * (uint32_t)crow), 0x00020000);
+    const int nb = wave < nblk ? (nblk - 1 - wave) / 4 + 1 : 0;   // this wave's blocks
+
+    // Loads of the wave's i-th block (block wave + 4 i): the lane's weight piece and its codes of
+    // the five digit slabs.  Past the wave's last block the offsets leave the buffer ranges and
+    // the loads return zeros, so every load is unconditional.  A slab past K (whose trits are
+    // 0) reads the row's last codes instead, so no load leaves its row.
+    typedef typename std::conditional<BITS == 8, u4, u2>::type CodeVec;
+    struct Slot {
+        u4 w[1];
+        CodeVec x[5];
+    };
+    constexpr uint32_t CB = BITS == 8 ? 16u : 8u;        // code bytes per lane and slab
+    const uint32_t rowoff = (uint32_t)(lane & 15) * (uint32_t)crow;
+    const uint32_t clast = (uint32_t)crow - CB;
+    const uint32_t kOut = 0x80000000u;
+    auto load = [&](Slot& s, int i) {
+        // past = 2^31 when i >= nb, else 0 (the sign of nb - 1 - i; arithmetic rather than a
+        // select, which the compiler would turn into branches around the loads)
+        const uint32_t past = (uint32_t)(nb - 1 - i) & kOut;
+        const uint32_t B = (uint32_t)(wave + 4 * i);
+        s.w[0] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(1024u * B + 16u * lane + past), 0, kNonTemporal);
+#pragma unroll
+        for (int d = 0; d < 5; d++) {
+            const uint32_t k0 = 320u * B + 64u * d + 16u * g;
+            const uint32_t o = rowoff + min(BITS == 8 ? k0 : k0 / 2, clast) + past;
+            if constexpr (BITS == 8) s.x[d] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)o, 0, 0);
+            else s.x[d] = __builtin_amdgcn_raw_buffer_load_b64(crs, (int)o, 0, 0);
+        }
+    };
+    auto codes = [&](const Slot& s, u4 (&d)[5]) {
+#pragma unroll
+        for (int i = 0; i < 5; i++) {
+            if constexpr (BITS == 8) {
+                d[i] = s.x[i];
+            } else {
+                const u2 v = s.x[i];
+                d[i] = u4{sext_nibbles(v[0] & 0x0F0F0F0Fu), sext_nibbles((v[0] >> 4) & 0x0F0F0F0Fu),
+                          sext_nibbles(v[1] & 0x0F0F0F0Fu), sext_nibbles((v[1] >> 4) & 0x0F0F0F0Fu)};
+            }
+        }
+    };
+
+    Slot s0, s1, s2, s3;
+    load(s0, 0);
+    load(s1, 1);
+    load(s2, 2);
+    load(s3, 3);
+    build_table(lut, tid);
+
+    const uint32_t laneoff = 8u * (uint32_t)(lane & 31);
+    constexpr int LA = kLookahead;
+    v4i acc[1] = {v4i{0, 0, 0, 0}};
+    v4i bn[LA];
+#pragma unroll
+    for (int i = 0; i < LA; i++) bn[i] = lookup_operand<1>(lut, laneoff, s0.w, i);
+    // Step i: the MFMAs of block i, the loads of block i + 4 into the freed slot, the first
+    // lookups of block i + 1.
+    auto step = [&](Slot& s, const Slot& sn, int i) {
+        u4 d[5];
+        codes(s, d);
+        block_mfmas<1, LA>(lut, laneoff, d, s.w, bn, acc);
+        load(s, i + 4);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < LA; q++) bn[q] = lookup_operand<1>(lut, laneoff, sn.w, q);
+    };
+    int i = 0;
+    for (; i + 4 <= nb; i += 4) {
+        step(s0, s1, i);
+        step(s1, s2, i + 1);
+        step(s2, s3, i + 2);
+        step(s3, s0, i + 3);
+    }
+    if (i < nb) step(s0, s1, i);
+    if (i + 1 < nb) step(s1, s2, i + 1);
+    if (i + 2 < nb) step(s2, s3, i + 2);
+
+    // Sum of the four partial tiles: thread (wave r, lane l) forms register r of lane l, i.e.
+    // output row 4 (l >> 4) + r, column l & 15 of the group.
+    *reinterpret_cast<v4i*>(&part[4 * (64 * wave + lane)]) = acc[0];
+    __syncthreads();
+    int32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) sum += part[4 * (64 * w + lane) + wave];
+    const int m = 4 * g + wave, n = 16 * gi + (lane & 15);
+    void* obase = DEQ ? (void*)(a.out + (int64_t)l * M * N) : (void*)(a.acc + (int64_t)l * M * N);
+    const auto os = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 4 * M * N, 0x00020000);
+    uint32_t o = 4u * ((uint32_t)m * (uint32_t)N + (uint32_t)n);
+    o = m < M && n < N ? o : kOut;
+    uint32_t v;
+    if constexpr (DEQ) {
+        const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t)l * M), 0, 4 * M, 0x00020000);
+        const float sx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * m, 0, 0));
+        const float ws = layer_scale(a.wscales, a.wscale0, l);
+        v = __builtin_bit_cast(uint32_t, ((float)sum * sx) * ws);
+    } else {
+        v = (uint32_t)sum;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, kNonTemporal);
+}
+
+enum class DecodeKind { Wide, Narrow, SplitK };
+
+template <int BITS, bool DEQ>
+void launch_decode(DecodeKind kind, int grid, const DecodeArgs& a, hipStream_t stream)
+{
+    if (kind == DecodeKind::Wide)
+        hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4>), dim3(grid), dim3(DT), 0, stream, a);
+    else if (kind == DecodeKind::Narrow)
+        hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1>), dim3(grid), dim3(DT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_decode_splitk_kernel<BITS, DEQ>), dim3(grid), dim3(DT), 0, stream, a);
 }
 
 }  // namespace
@@ -423,17 +586,31 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N};
+    // Enough 256-row items to give every CU one: the streaming kernel with four tiles per wave.
+    // Else, when the 16-row groups fit two workgroups per CU: one workgroup per group, K split
+    // over its waves.  Else the streaming kernel with one tile per wave (64-row items).
     const int cus = device_cus();
     const int items4 = L * ((N + wg_rows(4) - 1) / wg_rows(4));
-    const bool wide = items4 >= cus;
-    const int items = wide ? items4 : L * ((N + wg_rows(1) - 1) / wg_rows(1));
-    const int grid = items < 2 * cus ? items : 2 * cus;
-    if (out_f32 != nullptr) {
-        if (bits == 8) launch_decode<8, true>(wide, grid, a, stream);
-        else launch_decode<4, true>(wide, grid, a, stream);
+    const int groups = L * ((N + 15) / 16);
+    DecodeKind kind;
+    int grid;
+    if (items4 >= cus) {
+        kind = DecodeKind::Wide;
+        grid = items4 < 2 * cus ? items4 : 2 * cus;
+    } else if (groups <= 2 * cus) {
+        kind = DecodeKind::SplitK;
+        grid = groups;
     } else {
-        if (bits == 8) launch_decode<8, false>(wide, grid, a, stream);
-        else launch_decode<4, false>(wide, grid, a, stream);
+        kind = DecodeKind::Narrow;
+        const int items1 = L * ((N + wg_rows(1) - 1) / wg_rows(1));
+        grid = items1 < 2 * cus ? items1 : 2 * cus;
+    }
+    if (out_f32 != nullptr) {
+        if (bits == 8) launch_decode<8, true>(kind, grid, a, stream);
+        else launch_decode<4, true>(kind, grid, a, stream);
+    } else {
+        if (bits == 8) launch_decode<8, false>(kind, grid, a, stream);
+        else launch_decode<4, false>(kind, grid, a, stream);
     }
     return hipGetLastError();
 }

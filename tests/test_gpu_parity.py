@@ -318,6 +318,42 @@ def test_decode_kernel_gemm_i32(tb, M, bits):
     np.testing.assert_array_equal(acc.cpu().numpy(), oracle.gemm(q, oracle.unpack(packed, N, K)))
 
 
+# Decode shapes (M <= 16) run one of three kernels, chosen by the work items a call makes on a
+# 256-CU device: 256-row streaming items when there are at least 256 of them; else one
+# workgroup per 16-row group, K split over its four waves, when there are at most 512 groups;
+# else 64-row streaming items.  Each case lands on one of them; the K values give waves with no
+# block, uneven block counts and more than four blocks per wave.
+@pytest.mark.parametrize("L,M,K,N,bits", [
+    (1, 16, 16384, 1000, 4),    # split K: 52 blocks, 13 per wave
+    (1, 7, 8192, 4100, 8),      # split K: 26 blocks (7, 7, 6, 6 per wave), ragged N
+    (2, 2, 256, 200, 8),        # split K: one block, three idle waves
+    (3, 9, 960, 300, 4),        # split K: three blocks, one idle wave
+    (1, 16, 2048, 12000, 8),    # 64-row items: 750 groups
+    (2, 5, 4096, 8200, 4),      # 64-row items over two layers
+    (20, 3, 1024, 4096, 8),     # 256-row items: 320 of them
+])
+def test_decode_paths_match_oracle(tb, L, M, K, N, bits):
+    say(f"  decode path L={L} M={M} K={K} N={N} bits={bits}")
+    qp = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(L * 100003 + M * 101 + K + N + bits)
+    q = rng.integers(-qp - 1, qp + 1, size=(L, M, K)).astype(np.int8)
+    sx = rng.uniform(1e-3, 1e-1, size=(L, M)).astype(np.float32)
+    packs, gs, ts = [], [], []
+    for l in range(L):
+        packed, g = tb.bitnet_pack_weights(si.gaussian_weights(9, N, K, layer=l))
+        packs.append(dev(packed)); gs.append(g); ts.append(oracle.unpack(packed, N, K))
+    ptrs = torch.tensor([p.data_ptr() for p in packs], dtype=torch.int64, device="cuda")
+    wsc = torch.tensor(gs, dtype=torch.float32, device="cuda")
+    cb = [q[l].view(np.uint8) if bits == 8 else oracle.pack_int4(q[l]) for l in range(L)]
+    codes = dev(np.concatenate([c.reshape(-1) for c in cb]))
+    y = tb.hbitlinear_gemm_dequant_grouped(codes, dev(sx.reshape(-1)), L, M, K, N, bits, ptrs, wsc)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    for l in range(L):
+        oy = oracle.epilogue(oracle.gemm(q[l], ts[l]), sx[l], np.float32(gs[l]))
+        np.testing.assert_array_equal(yh[l], oy, err_msg=f"layer {l}")
+
+
 # -------------------------------------------------------------------- graph capture ----
 
 @pytest.mark.parametrize("L,M,K,N,bits,had", [(4, 16, 4096, 512, 8, False), (1, 600, 4096, 384, 4, True)])
