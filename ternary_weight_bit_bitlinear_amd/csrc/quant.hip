@@ -196,9 +196,10 @@ __global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
     using G = Geometry<L>;
     constexpr int K = G::K, T = G::T, E = G::E;
     constexpr int QP = (1 << (BITS - 1)) - 1;
-    __shared__ __align__(16) float lds[K];
-    // Reduction slots sit past the K code bytes that are written after the reduction.
-    float* red = lds + K / 2;
+    // With the transform: the row for the exchanges, then the code bytes; the reduction slots
+    // sit past the K code bytes.  Without: only the reduction slots.
+    __shared__ __align__(16) float lds[HAD ? K : 64];
+    float* red = HAD ? lds + K / 2 : lds;
 
     const uint32_t t = threadIdx.x;
     const int64_t m = blockIdx.x;
@@ -241,6 +242,30 @@ __global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
 
     const float inv = g > 0.0f ? (float)QP / g : 0.0f;   // IEEE division
     if (t == 0) scales[m] = g > 0.0f ? g / (float)QP : 0.0f;
+
+    if constexpr (!HAD) {
+        // Load layout A: register 4 r + j holds k = 4 T r + 4 t + j, so the four codes of a
+        // float4 are consecutive: INT8, one 4-byte store; INT4, the four nibbles of this
+        // thread (low nibbles of word k / 8 when t is even, high when odd) joined with the
+        // neighbour's, and stored by the even thread.
+#pragma unroll
+        for (int r = 0; r < E / 4; r++) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int q = g > 0.0f ? quant_code<BITS>(v[4 * r + j], inv) : 0;
+                if constexpr (BITS == 8) w |= (uint32_t)(q & 255) << (8 * j);
+                else w |= (uint32_t)(q & 15) << (8 * j + 4 * (t & 1));
+            }
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<uint32_t*>(codes + m * K + 4 * T * r + 4 * t) = w;
+            } else {
+                w |= (uint32_t)__shfl_xor((int)w, 1, 64);
+                if ((t & 1) == 0) *reinterpret_cast<uint32_t*>(codes + m * (K / 2) + 2 * T * r + 2 * t) = w;
+            }
+        }
+        return;
+    }
 
     // Codes into LDS as bytes at position k, then out with 16-byte stores.
     int8_t* qb = reinterpret_cast<int8_t*>(lds);

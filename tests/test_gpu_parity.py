@@ -86,6 +86,19 @@ def test_quantize_all_widths(tb, K, bits, had):
     check_quant(tb, x, bits, had, label=f"K={K} bits={bits} had={had}")
 
 
+# Many rows: more workgroups than the chip holds at once at every width (at most 160 KB / 4K
+# bytes of LDS per workgroup with the transform, 256 CUs), row counts that are not multiples of
+# anything the launch uses; sampled rows, including the first and last, against the oracle.
+@pytest.mark.parametrize("M,K,bits,had", [(7757, 4096, 4, True), (7757, 4096, 8, False),
+                                          (3001, 8192, 8, True), (1500, 16384, 4, True)])
+def test_quantize_many_rows(tb, M, K, bits, had):
+    x = si.wo_activations(M, K)
+    x[M - 1] = 0.0                    # last row zero: codes 0, scale 0
+    rng = np.random.default_rng(M + K)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.choice(M, 48, replace=False)]))
+    check_quant(tb, x, bits, had, rows=rows, label=f"many rows M={M} K={K} bits={bits} had={had}")
+
+
 @pytest.mark.parametrize("K", [64, 320, 960, 4032])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_quantize_generic_widths(tb, K, bits):
