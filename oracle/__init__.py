@@ -68,6 +68,12 @@ def lib():
         L.bitnet_ref_epilogue.argtypes = [P, P, F, I, I, P]; L.bitnet_ref_epilogue.restype = None
         L.bitnet_ref_forward.argtypes = [P, I, I, I, I, I, P, F, P]
         L.bitnet_ref_forward.restype = I
+        L.bitnet_ref_forward_segments.argtypes = [P, I, I, I, P, I, I, P, P, P]
+        L.bitnet_ref_forward_segments.restype = I
+        L.bitnet_ref_silu.argtypes = [F]; L.bitnet_ref_silu.restype = F
+        L.bitnet_ref_swiglu.argtypes = [P, P, I64, P]; L.bitnet_ref_swiglu.restype = None
+        L.bitnet_ref_forward_swiglu.argtypes = [P, I, I, I, I, I, P, F, P, F, P]
+        L.bitnet_ref_forward_swiglu.restype = I
         L.bitnet_ref_num_threads.argtypes = []; L.bitnet_ref_num_threads.restype = I
         L.bitnet_ref_set_num_threads.argtypes = [I]; L.bitnet_ref_set_num_threads.restype = None
         _lib = L
@@ -247,6 +253,53 @@ def forward(x, packed, gamma_w, N: int, bits: int, use_hadamard: bool):
     if rc != 0:
         raise ValueError("packed buffer does not decode")
     return y
+
+
+def forward_segments(x, packs, gammas, seg_n, bits: int, use_hadamard: bool):
+    """Several linears of one input: y = [forward(x, packs[s], gammas[s]) for s] side by side
+    (M x sum(seg_n)); packs are separately packed matrices."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    S = len(seg_n)
+    bufs = [_c(p, np.uint8) for p in packs]
+    ptrs = (ctypes.c_void_p * S)(*[b.ctypes.data for b in bufs])
+    n = np.asarray(seg_n, np.int32)
+    g = np.asarray(gammas, np.float32)
+    y = np.empty((M, int(n.sum())), np.float32)
+    rc = lib().bitnet_ref_forward_segments(_p(x), M, K, S, _p(n), bits, int(bool(use_hadamard)),
+                                           ctypes.cast(ptrs, ctypes.c_void_p), _p(g), _p(y))
+    if rc != 0:
+        raise ValueError("packed buffer does not decode")
+    return y
+
+
+def silu(z) -> np.float32:
+    return np.float32(lib().bitnet_ref_silu(float(z)))
+
+
+def swiglu(g, u):
+    """h = SiLU(g) * u elementwise (double arithmetic, one rounding to fp32)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, np.float32)
+    lib().bitnet_ref_swiglu(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def forward_swiglu(x, packed_gate, gamma_gate, packed_up, gamma_up, F: int, bits: int,
+                   use_hadamard: bool):
+    """h (M x F) = SwishGLU of the gate and up forwards of x."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    pg = _c(packed_gate, np.uint8)
+    pu = _c(packed_up, np.uint8)
+    h = np.empty((M, F), np.float32)
+    rc = lib().bitnet_ref_forward_swiglu(_p(x), M, K, F, bits, int(bool(use_hadamard)), _p(pg),
+                                         float(gamma_gate), _p(pu), float(gamma_up), _p(h))
+    if rc != 0:
+        raise ValueError("packed buffer does not decode")
+    return h
 
 
 def num_threads() -> int:

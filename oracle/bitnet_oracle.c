@@ -328,6 +328,67 @@ int bitnet_ref_forward(const float *x, int M, int K, int N, int bits, int use_ha
     return rc;
 }
 
+/* ------------------------------------------------------------------------------------- */
+/* Several linears that read the same input (for instance Q, K and V of a block), each with  */
+/* its own packed weights and weight scale: y is M x (N_0 + ... + N_{S-1}), segment s in the */
+/* columns that follow segments 0 .. s-1, each exactly bitnet_ref_forward of that matrix.     */
+/* packed: S pointers to separately packed matrices (N_s x K each).                          */
+/* ------------------------------------------------------------------------------------- */
+int bitnet_ref_forward_segments(const float *x, int M, int K, int S, const int *seg_n, int bits,
+                                int use_hadamard, const uint8_t *const *packed,
+                                const float *gammas, float *y)
+{
+    int ntot = 0;
+    for (int s = 0; s < S; s++) ntot += seg_n[s];
+    int rc = 0, col = 0;
+    for (int s = 0; s < S && rc == 0; s++) {
+        const int N = seg_n[s];
+        float *ys = (float *)malloc(sizeof(float) * (size_t)M * (size_t)N);
+        rc = bitnet_ref_forward(x, M, K, N, bits, use_hadamard, packed[s], gammas[s], ys);
+        for (int m = 0; m < M && rc == 0; m++)
+            memcpy(y + (int64_t)m * ntot + col, ys + (int64_t)m * N, sizeof(float) * (size_t)N);
+        free(ys);
+        col += N;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Gated feed-forward glue [v2-news: LLaMA-like components, among them the SwishGLU          */
+/* activation].  Reading taken: Swish with beta = 1, i.e. SiLU(z) = z * sigmoid(z) =          */
+/* z / (1 + e^-z), and SwishGLU(x) = SiLU(x W_gate^T) (elementwise product) (x W_up^T), the    */
+/* two products being two BitLinear forwards of the same input.  The pages fix no precision  */
+/* for the glue; it is evaluated in double and rounded to fp32 once.                          */
+/* ------------------------------------------------------------------------------------- */
+float bitnet_ref_silu(float z)
+{
+    const double d = (double)z;
+    return (float)(d / (1.0 + exp(-d)));
+}
+
+void bitnet_ref_swiglu(const float *g, const float *u, int64_t count, float *h)
+{
+    for (int64_t i = 0; i < count; i++) {
+        const double d = (double)g[i];
+        h[i] = (float)((d / (1.0 + exp(-d))) * (double)u[i]);
+    }
+}
+
+/* h (M x F) = SwishGLU of the gate and up forwards of x (each a bitnet_ref_forward with its  */
+/* own packed F x K matrix and weight scale).                                                */
+int bitnet_ref_forward_swiglu(const float *x, int M, int K, int F, int bits, int use_hadamard,
+                              const uint8_t *packed_gate, float gamma_gate,
+                              const uint8_t *packed_up, float gamma_up, float *h)
+{
+    float *g = (float *)malloc(sizeof(float) * (size_t)M * (size_t)F);
+    float *u = (float *)malloc(sizeof(float) * (size_t)M * (size_t)F);
+    int rc = bitnet_ref_forward(x, M, K, F, bits, use_hadamard, packed_gate, gamma_gate, g);
+    if (rc == 0) rc = bitnet_ref_forward(x, M, K, F, bits, use_hadamard, packed_up, gamma_up, u);
+    if (rc == 0) bitnet_ref_swiglu(g, u, (int64_t)M * F, h);
+    free(g); free(u);
+    return rc;
+}
+
 /* Number of OpenMP threads a parallel region here uses (1 without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

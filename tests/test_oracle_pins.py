@@ -346,3 +346,110 @@ def test_forward_is_composition_of_stages():
     xh = oracle.hadamard(x)
     kurt = lambda v: np.mean(v ** 4, axis=1) / np.mean(v ** 2, axis=1) ** 2
     assert np.all(kurt(xh) < kurt(x))
+
+
+# ------------------------------------------------------- several linears, one input ----
+
+def test_forward_segments_hadamard_row_closed_form():
+    # Three linears with their own weights and scales on x = a * H[j, :]: each segment's
+    # columns follow the single-linear closed form a sqrt(K) t_s[n, j] gamma_s.
+    K = 1024
+    seg_n = [48, 16, 32]
+    H = oracle.fwht(np.eye(K, dtype=np.float32))
+    packs, gammas, ts = [], [], []
+    for s, n in enumerate(seg_n):
+        packed, g, t = oracle.pack_weights(si.gaussian_weights(6, n, K, layer=s, std=0.02 * (s + 1)))
+        packs.append(packed); gammas.append(g); ts.append(t)
+    assert len(set(float(g) for g in gammas)) == 3
+    for j, a in ((3, 1.25), (K - 2, -0.5)):
+        x = (np.float32(a) * H[j])[None, :]
+        y = oracle.forward_segments(x, packs, gammas, seg_n, 4, True)
+        assert y.shape == (1, sum(seg_n))
+        expect = np.concatenate([a * math.sqrt(K) * t[:, j].astype(np.float64) * float(g)
+                                 for t, g in zip(ts, gammas)])
+        assert np.allclose(y[0], expect, rtol=1e-6, atol=0)
+
+
+def test_forward_segments_integer_grid_exact():
+    # integer-grid input (s = 1): every segment is gamma_s * (x t_s^T) exactly, in its columns
+    rng = np.random.default_rng(12)
+    M, K = 3, 640
+    x = rng.integers(-127, 128, size=(M, K)).astype(np.float32); x[:, 7] = -127
+    seg_n = [16, 40]
+    packs, gammas, ts = [], [], []
+    for s, n in enumerate(seg_n):
+        packed, g, t = oracle.pack_weights(si.gaussian_weights(7, n, K, layer=s))
+        packs.append(packed); gammas.append(g); ts.append(t)
+    y = oracle.forward_segments(x, packs, gammas, seg_n, 8, False)
+    exact = np.concatenate([(x.astype(np.int64) @ t.astype(np.int64).T).astype(np.float32) * g
+                            for t, g in zip(ts, gammas)], axis=1)
+    assert np.array_equal(y, exact)
+
+
+# ------------------------------------------------------------------ SwishGLU glue ----
+
+def test_silu_textbook_values_and_identities():
+    # SiLU(z) = z sigmoid(z): SiLU(0) = 0, SiLU(1) = sigmoid(1) = 1 / (1 + 1/e)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == np.float32(1.0 / (1.0 + math.exp(-1.0)))
+    assert abs(float(oracle.silu(1.0)) - 0.7310585786300049) < 1e-7
+    # SiLU(z) - SiLU(-z) = z (sigmoid(z) + sigmoid(-z) = 1)
+    for z in np.linspace(-12, 12, 97):
+        d = float(oracle.silu(z)) - float(oracle.silu(-z))
+        assert abs(d - float(np.float32(z))) <= 4e-7 * max(1.0, abs(z))
+    # tails: -> z for large z, -> 0 from below for very negative z
+    assert oracle.silu(40.0) == np.float32(40.0)
+    assert -1e-15 < float(oracle.silu(-40.0)) < 0.0
+
+
+def test_silu_minimum_is_lambert_w():
+    # d/dz z sigmoid(z) = 0 at z* = -(1 + W(1/e)); the minimum value is z* + 1 = -W(1/e)
+    from scipy.special import lambertw
+    w = float(lambertw(1.0 / math.e).real)
+    zs = np.linspace(-1.35, -1.2, 30001).astype(np.float32)
+    vals = np.array([float(oracle.silu(z)) for z in zs])
+    i = int(np.argmin(vals))
+    # near z* the curve is flat to within fp32 resolution of the values (f'' ~ 0.2, an ulp of
+    # 0.28 is 3e-8), so the location is pinned to about 1e-3 and the value to 1e-7
+    assert abs(float(zs[i]) + 1.0 + w) < 1e-3
+    assert abs(vals[i] + w) < 1e-7
+
+
+def test_swiglu_elementwise_matches_definition_and_zeros():
+    rng = np.random.default_rng(13)
+    g = rng.normal(0, 3, size=(5, 64)).astype(np.float32)
+    u = rng.normal(0, 2, size=(5, 64)).astype(np.float32)
+    h = oracle.swiglu(g, u)
+    gd = g.astype(np.float64)
+    ref = (gd / (1.0 + np.exp(-gd)) * u.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(h, ref)
+    assert np.all(oracle.swiglu(np.zeros_like(g), u) == 0)
+    assert np.all(oracle.swiglu(g, np.zeros_like(u)) == 0)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_swiglu_hadamard_row_closed_form(bits):
+    # x = a * H[j, :]: gate and up each follow the single-linear closed form, so
+    # h[n] = SiLU(a sqrt(K) t_g[n, j] gamma_g) * a sqrt(K) t_u[n, j] gamma_u
+    K, F = 1024, 48
+    H = oracle.fwht(np.eye(K, dtype=np.float32))
+    pg, gg, tg = oracle.pack_weights(si.gaussian_weights(8, F, K, layer=0))
+    pu, gu, tu = oracle.pack_weights(si.gaussian_weights(8, F, K, layer=1, std=0.05))
+    for j, a in ((1, 0.5), (K - 3, -2.0)):
+        x = (np.float32(a) * H[j])[None, :]
+        h = oracle.forward_swiglu(x, pg, gg, pu, gu, F, bits, True)
+        gv = a * math.sqrt(K) * tg[:, j].astype(np.float64) * float(gg)
+        uv = a * math.sqrt(K) * tu[:, j].astype(np.float64) * float(gu)
+        expect = gv / (1.0 + np.exp(-gv)) * uv
+        assert np.allclose(h[0], expect, rtol=1e-6, atol=1e-12)
+
+
+def test_forward_swiglu_zero_gate_or_up_gives_zero():
+    rng = np.random.default_rng(14)
+    M, K, F = 4, 512, 32
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    pz, gz, _ = oracle.pack_weights(np.zeros((F, K), np.float32))
+    pw, gw, _ = oracle.pack_weights(si.gaussian_weights(9, F, K))
+    assert gz == 0
+    assert np.all(oracle.forward_swiglu(x, pz, gz, pw, gw, F, 8, True) == 0)
+    assert np.all(oracle.forward_swiglu(x, pw, gw, pz, gz, F, 8, True) == 0)
