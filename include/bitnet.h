@@ -84,6 +84,27 @@ int bitnet_packed_bytes(int N, int K, size_t *bytes_out);
 int bitnet_pack_weights(const float *W_host, int N, int K, uint8_t *packed_host,
                         float *w_scale_out);
 
+/* Most weight matrices one packed buffer can stack (bitnet_pack_weights_segments). */
+#define BITNET_MAX_SEGMENTS 8
+
+/* Several linears that read the same input -- e.g. the Q, K and V projections of a block --
+ * prepared for one product launch: W_host stacks S matrices by rows (seg_n[s] x K each,
+ * host, seg_n[s] a multiple of 16, 1 <= S <= BITNET_MAX_SEGMENTS); each is ternarised with
+ * its own absmean scale (w_scales_out[s], host) exactly as bitnet_pack_weights, and the packed
+ * matrices follow one another in packed_host (bitnet_packed_bytes(sum seg_n, K) bytes: whole
+ * 16-row groups, so the result is the packed layout of the stacked matrix). */
+int bitnet_pack_weights_segments(const float *W_host, int S, const int *seg_n, int K,
+                                 uint8_t *packed_host, float *w_scales_out);
+
+/* Gate and up projections of a gated feed-forward [v2 write-up: LLaMA-like components,
+ * among them the SwishGLU activation], prepared for one product launch with the glue fused:
+ * W_gate_host and W_up_host are F x K (host, F a multiple of 16), each ternarised with its own
+ * absmean scale exactly as bitnet_pack_weights; packed_host (bitnet_packed_bytes(2 F, K)
+ * bytes) interleaves them by 16-row groups: group 2i holds gate rows 16i..16i+15, group 2i+1
+ * the same up rows.  Uses a host copy of one packed matrix while interleaving. */
+int bitnet_pack_gate_up(const float *W_gate_host, const float *W_up_host, int F, int K,
+                        uint8_t *packed_host, float *gate_scale_out, float *up_scale_out);
+
 /* Inverse of the packing: trits_host (N x K int8, host) receives t in {-1, 0, +1}.
  * Returns BITNET_ERR_FORMAT if a byte is > 242 or a padding position is not t = 0. */
 int bitnet_unpack_weights(const uint8_t *packed_host, int N, int K, int8_t *trits_host);
@@ -121,6 +142,32 @@ int hbitlinear_forward_grouped(int L, const float *x, int M, int K, int N, int a
                                int use_hadamard, float *out, const uint8_t *const *packed_ws,
                                const float *w_scales, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* Several linears of one input in one call: x's activation stage runs once, then one product
+ * launch covers the S stacked matrices of bitnet_pack_weights_segments:
+ *   out[m][c] = forward(x, matrix s, w_scales[s])[m][c - c_s] for the columns
+ *   c_s <= c < c_s + seg_n[s] of segment s (c_s = seg_n[0] + ... + seg_n[s-1]),
+ * each exactly as hbitlinear_forward.  seg_n and w_scales are host arrays of S entries;
+ * x (M x K), out (M x sum seg_n), packed_w and workspace (hbitlinear_workspace_bytes(M, K,
+ * act_bits)) are device pointers.  Shape rules as hbitlinear_forward with N = sum seg_n,
+ * plus seg_n[s] % 16 == 0 and 1 <= S <= BITNET_MAX_SEGMENTS. */
+int hbitlinear_forward_segments(const float *x, int M, int K, int S, const int *seg_n,
+                                int act_bits, int use_hadamard, float *out,
+                                const uint8_t *packed_w, const float *w_scales, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Gated feed-forward input projections with the SwishGLU glue in the product's epilogue
+ * [v2 write-up: SwishGLU; reading taken: Swish with beta = 1, SiLU(z) = z / (1 + e^-z)]:
+ *   g = forward(x, gate), u = forward(x, up)   (each exactly as hbitlinear_forward)
+ *   h[m][f] = SiLU(g[m][f]) * u[m][f]          (fp32; SiLU with the device expf and an IEEE
+ *                                               division, so within a few ulp of the exact value)
+ * packed_gate_up as bitnet_pack_gate_up; h is M x F fp32; x, h, packed_gate_up and workspace
+ * (hbitlinear_workspace_bytes(M, K, act_bits)) are device pointers.  Neither g nor u is
+ * written to memory.  Shape rules as hbitlinear_forward with N = 2 F, plus F % 16 == 0. */
+int hbitlinear_forward_swiglu(const float *x, int M, int K, int F, int act_bits,
+                              int use_hadamard, float *h, const uint8_t *packed_gate_up,
+                              float gate_scale, float up_scale, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* The two stages of the forward, exported so each can be checked and timed on its own.  */
@@ -161,6 +208,16 @@ int hbitlinear_gemm_dequant(const uint8_t *codes, const float *scales, int M, in
 int hbitlinear_gemm_dequant_grouped(const uint8_t *codes, const float *scales, int L, int M,
                                     int K, int N, int act_bits, const uint8_t *const *packed_ws,
                                     const float *w_scales, float *out, void *stream);
+
+/* The product stages of hbitlinear_forward_segments and hbitlinear_forward_swiglu, from codes
+ * and scales as written by hbitlinear_quantize (device); seg_n, w_scales host arrays. */
+int hbitlinear_gemm_dequant_segments(const uint8_t *codes, const float *scales, int M, int K,
+                                     int S, const int *seg_n, int act_bits,
+                                     const uint8_t *packed_w, const float *w_scales, float *out,
+                                     void *stream);
+int hbitlinear_gemm_swiglu(const uint8_t *codes, const float *scales, int M, int K, int F,
+                           int act_bits, const uint8_t *packed_gate_up, float gate_scale,
+                           float up_scale, float *h, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,4 +11,6 @@ from .bitnet import (  # noqa: F401
     bitnet_ternary_gemm_i32, bitnet_unpack_weights, hbitlinear_codes_bytes, hbitlinear_forward,
     hbitlinear_forward_grouped, hbitlinear_gemm_dequant, hbitlinear_gemm_dequant_grouped,
     hbitlinear_grouped_workspace_bytes, hbitlinear_quantize, hbitlinear_workspace_bytes, lib,
+    bitnet_pack_gate_up, bitnet_pack_weights_segments, hbitlinear_forward_segments,
+    hbitlinear_forward_swiglu, hbitlinear_gemm_dequant_segments, hbitlinear_gemm_swiglu,
 )

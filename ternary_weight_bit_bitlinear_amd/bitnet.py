@@ -57,6 +57,12 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_grouped_workspace_bytes": ([I, I, I, I, PSZ], I),
             "hbitlinear_forward_grouped": ([I, P, I, I, I, I, I, P, P, P, P, SZ, P], I),
             "hbitlinear_gemm_dequant_grouped": ([P, P, I, I, I, I, I, P, P, P, P], I),
+            "bitnet_pack_weights_segments": ([P, I, P, I, P, P], I),
+            "bitnet_pack_gate_up": ([P, P, I, I, P, P, P], I),
+            "hbitlinear_forward_segments": ([P, I, I, I, P, I, I, P, P, P, P, SZ, P], I),
+            "hbitlinear_gemm_dequant_segments": ([P, P, I, I, I, P, I, P, P, P, P], I),
+            "hbitlinear_forward_swiglu": ([P, I, I, I, I, I, P, P, F, F, P, SZ, P], I),
+            "hbitlinear_gemm_swiglu": ([P, P, I, I, I, I, P, F, F, P, P], I),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -142,6 +148,37 @@ def bitnet_pack_weights(W):
     return packed, float(g.value)
 
 
+def bitnet_pack_weights_segments(W, seg_n):
+    """Pack S matrices stacked by rows in W (sum(seg_n) x K fp32, host), each with its own
+    absmean scale -> (packed uint8, w_scales float32 array of S)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    n = np.ascontiguousarray(seg_n, dtype=np.int32)
+    S = n.size
+    rows, K = W.shape
+    if int(n.sum()) != rows:
+        raise ValueError("W must have sum(seg_n) rows")
+    packed = np.empty(bitnet_packed_bytes(rows, K), np.uint8)
+    g = np.zeros(S, np.float32)
+    _check(lib().bitnet_pack_weights_segments(_ptr(W), S, _ptr(n), K, _ptr(packed), _ptr(g)),
+           "bitnet_pack_weights_segments")
+    return packed, g
+
+
+def bitnet_pack_gate_up(W_gate, W_up):
+    """Pack the gate and up matrices (F x K fp32 each, host), interleaved by 16-row groups ->
+    (packed uint8, gate_scale, up_scale)."""
+    Wg = np.ascontiguousarray(W_gate, dtype=np.float32)
+    Wu = np.ascontiguousarray(W_up, dtype=np.float32)
+    if Wg.shape != Wu.shape:
+        raise ValueError("gate and up must have the same shape")
+    F, K = Wg.shape
+    packed = np.empty(bitnet_packed_bytes(2 * F, K), np.uint8)
+    gg, gu = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    _check(lib().bitnet_pack_gate_up(_ptr(Wg), _ptr(Wu), F, K, _ptr(packed), ctypes.byref(gg),
+                                     ctypes.byref(gu)), "bitnet_pack_gate_up")
+    return packed, float(gg.value), float(gu.value)
+
+
 def bitnet_unpack_weights(packed, N: int, K: int):
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     t = np.empty((N, K), np.int8)
@@ -170,6 +207,66 @@ def hbitlinear_forward(x, N: int, act_bits: int, use_hadamard: bool, packed_w, w
     _check(lib().hbitlinear_forward(_ptr(x), M, K, N, act_bits, int(bool(use_hadamard)),
                                     _ptr(out), _ptr(packed_w), float(w_scale), _ptr(workspace),
                                     workspace.numel(), _stream(stream)), "hbitlinear_forward")
+    return out
+
+
+def _seg_arrays(seg_n, w_scales):
+    n = np.ascontiguousarray(seg_n, dtype=np.int32)
+    g = np.ascontiguousarray(w_scales, dtype=np.float32)
+    if g.size != n.size:
+        raise ValueError("seg_n and w_scales need the same number of entries")
+    return n, g
+
+
+def hbitlinear_forward_segments(x, seg_n, act_bits: int, use_hadamard: bool, packed_w, w_scales,
+                                out=None, workspace=None, stream=None):
+    """Several linears of one input: x (M x K fp32, device), packed_w from
+    bitnet_pack_weights_segments (device), seg_n / w_scales (host sequences of S) ->
+    out (M x sum(seg_n) fp32, device)."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    n, g = _seg_arrays(seg_n, w_scales)
+    M, K = x.shape
+    N = int(n.sum())
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * N:
+        raise ValueError("out is too small")
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_workspace_bytes(M, K, act_bits), dtype=torch.uint8,
+                                device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward_segments(_ptr(x), M, K, n.size, _ptr(n), act_bits,
+                                             int(bool(use_hadamard)), _ptr(out), _ptr(packed_w),
+                                             _ptr(g), _ptr(workspace), workspace.numel(),
+                                             _stream(stream)), "hbitlinear_forward_segments")
+    return out
+
+
+def hbitlinear_forward_swiglu(x, F: int, act_bits: int, use_hadamard: bool, packed_gate_up,
+                              gate_scale: float, up_scale: float, out=None, workspace=None,
+                              stream=None):
+    """h = SiLU(gate(x)) * up(x): x (M x K fp32, device), packed_gate_up from
+    bitnet_pack_gate_up (device) -> h (M x F fp32, device)."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_gate_up, torch.uint8, "packed_gate_up")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=x.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * F:
+        raise ValueError("out is too small")
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_workspace_bytes(M, K, act_bits), dtype=torch.uint8,
+                                device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward_swiglu(_ptr(x), M, K, F, act_bits, int(bool(use_hadamard)),
+                                           _ptr(out), _ptr(packed_gate_up), float(gate_scale),
+                                           float(up_scale), _ptr(workspace), workspace.numel(),
+                                           _stream(stream)), "hbitlinear_forward_swiglu")
     return out
 
 
@@ -284,4 +381,50 @@ def hbitlinear_gemm_dequant_grouped(codes, scales, L: int, M: int, K: int, N: in
     _check(lib().hbitlinear_gemm_dequant_grouped(_ptr(codes), _ptr(scales), L, M, K, N, act_bits,
                                                  _ptr(packed_ptrs), _ptr(w_scales), _ptr(out),
                                                  _stream(stream)), "hbitlinear_gemm_dequant_grouped")
+    return out
+
+
+def hbitlinear_gemm_dequant_segments(codes, scales, M: int, K: int, seg_n, act_bits: int,
+                                     packed_w, w_scales, out=None, stream=None):
+    """Product stage of hbitlinear_forward_segments from device codes and scales."""
+    import torch
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    n, g = _seg_arrays(seg_n, w_scales)
+    N = int(n.sum())
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    if packed_w.numel() < bitnet_packed_bytes(N, K):
+        raise ValueError("packed_w buffer is too small")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * N:
+        raise ValueError("out is too small")
+    _check(lib().hbitlinear_gemm_dequant_segments(_ptr(codes), _ptr(scales), M, K, n.size, _ptr(n),
+                                                  act_bits, _ptr(packed_w), _ptr(g), _ptr(out),
+                                                  _stream(stream)), "hbitlinear_gemm_dequant_segments")
+    return out
+
+
+def hbitlinear_gemm_swiglu(codes, scales, M: int, K: int, F: int, act_bits: int, packed_gate_up,
+                           gate_scale: float, up_scale: float, out=None, stream=None):
+    """Product stage of hbitlinear_forward_swiglu from device codes and scales -> h (M x F)."""
+    import torch
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    _dev_check(packed_gate_up, torch.uint8, "packed_gate_up")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    if packed_gate_up.numel() < bitnet_packed_bytes(2 * F, K):
+        raise ValueError("packed_gate_up buffer is too small")
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=codes.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * F:
+        raise ValueError("out is too small")
+    _check(lib().hbitlinear_gemm_swiglu(_ptr(codes), _ptr(scales), M, K, F, act_bits,
+                                        _ptr(packed_gate_up), float(gate_scale), float(up_scale),
+                                        _ptr(out), _stream(stream)), "hbitlinear_gemm_swiglu")
     return out

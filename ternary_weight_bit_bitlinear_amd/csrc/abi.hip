@@ -40,6 +40,36 @@ size_t workspace_bytes(int M, int K, int bits)
     return align256(codes_bytes(M, K, bits)) + align256((size_t)M * sizeof(float));
 }
 
+// Segments of a stacked weight (host arrays): checks them and fills the output form.
+int segment_form(int S, const int* seg_n, const float* w_scales, int* n_total, OutForm* of)
+{
+    if (seg_n == nullptr || w_scales == nullptr) return BITNET_ERR_NULL;
+    if (S <= 0 || S > BITNET_MAX_SEGMENTS || S > kMaxSegments) return BITNET_ERR_UNSUPPORTED;
+    int64_t rows = 0;
+    for (int s = 0; s < S; s++) {
+        if (seg_n[s] <= 0) return BITNET_ERR_SHAPE;
+        if (seg_n[s] % 16 != 0) return BITNET_ERR_UNSUPPORTED;
+        rows += seg_n[s];
+        of->seg_end[s] = (int)(rows / 16);
+        of->seg_scale[s] = w_scales[s];
+    }
+    if (rows > (int64_t)1 << 30) return BITNET_ERR_UNSUPPORTED;
+    of->nseg = S;
+    *n_total = (int)rows;
+    return BITNET_OK;
+}
+
+// Gate / up pairs of F rows each (F % 16 == 0): 2F weight rows, M x F output.
+int glu_form(int F, float gate_scale, float up_scale, OutForm* of)
+{
+    if (F <= 0) return BITNET_ERR_SHAPE;
+    if (F % 16 != 0 || F > (1 << 29)) return BITNET_ERR_UNSUPPORTED;
+    of->glu = 1;
+    of->gate_scale = gate_scale;
+    of->up_scale = up_scale;
+    return BITNET_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +159,83 @@ int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int us
     if (e != hipSuccess) return BITNET_ERR_HIP;
     return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
                                  w_scale, out, nullptr, s));
+}
+
+int hbitlinear_gemm_dequant_segments(const uint8_t* codes, const float* scales, int M, int K,
+                                     int S, const int* seg_n, int act_bits,
+                                     const uint8_t* packed_w, const float* w_scales, float* out,
+                                     void* stream)
+{
+    if (codes == nullptr || scales == nullptr || packed_w == nullptr || out == nullptr)
+        return BITNET_ERR_NULL;
+    OutForm of;
+    int N = 0;
+    int rc = segment_form(S, seg_n, w_scales, &N, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, N, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 0.0f, out, nullptr, (hipStream_t)stream, of));
+}
+
+int hbitlinear_forward_segments(const float* x, int M, int K, int S, const int* seg_n,
+                                int act_bits, int use_hadamard, float* out,
+                                const uint8_t* packed_w, const float* w_scales, void* workspace,
+                                size_t workspace_size, void* stream)
+{
+    if (x == nullptr || out == nullptr || packed_w == nullptr) return BITNET_ERR_NULL;
+    OutForm of;
+    int N = 0;
+    int rc = segment_form(S, seg_n, w_scales, &N, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 0.0f, out, nullptr, s, of));
+}
+
+int hbitlinear_gemm_swiglu(const uint8_t* codes, const float* scales, int M, int K, int F,
+                           int act_bits, const uint8_t* packed_gate_up, float gate_scale,
+                           float up_scale, float* h, void* stream)
+{
+    if (codes == nullptr || scales == nullptr || packed_gate_up == nullptr || h == nullptr)
+        return BITNET_ERR_NULL;
+    OutForm of;
+    int rc = glu_form(F, gate_scale, up_scale, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, 2 * F, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, 2 * F, act_bits);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_gemm(codes, 1, M, K, 2 * F, act_bits, nullptr, packed_gate_up, scales,
+                                 nullptr, 0.0f, h, nullptr, (hipStream_t)stream, of));
+}
+
+int hbitlinear_forward_swiglu(const float* x, int M, int K, int F, int act_bits,
+                              int use_hadamard, float* h, const uint8_t* packed_gate_up,
+                              float gate_scale, float up_scale, void* workspace,
+                              size_t workspace_size, void* stream)
+{
+    if (x == nullptr || h == nullptr || packed_gate_up == nullptr) return BITNET_ERR_NULL;
+    OutForm of;
+    int rc = glu_form(F, gate_scale, up_scale, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, 2 * F, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, 2 * F, act_bits);
+    if (rc != BITNET_OK) return rc;
+    if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, 1, M, K, 2 * F, act_bits, nullptr, packed_gate_up, scales,
+                                 nullptr, 0.0f, h, nullptr, s, of));
 }
 
 int hbitlinear_gemm_dequant_grouped(const uint8_t* codes, const float* scales, int L, int M,

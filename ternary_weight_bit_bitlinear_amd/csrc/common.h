@@ -24,6 +24,36 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Compute units of the current device, queried once per device (256 if the query fails).
 int device_cus();
 
+// Output form of a one-layer product launch beyond the plain epilogue (one weight scale):
+//  - segments: nseg weight matrices stacked by rows, segment s covering the 16-row groups
+//    [seg_end[s-1], seg_end[s]) (seg_end[-1] = 0) with weight scale seg_scale[s]; the output
+//    keeps one column per weight row;
+//  - glu: a gate matrix and an up matrix of F rows each, interleaved by 16-row groups (group
+//    2i = gate rows 16i..16i+15, group 2i+1 = the same up rows); the output is M x F,
+//    h = SiLU(gate) * up, each of gate and up dequantised with its own weight scale.
+// The default (nseg = 0, glu = 0) is the plain epilogue.
+constexpr int kMaxSegments = 8;
+struct OutForm {
+    int nseg = 0;
+    int seg_end[kMaxSegments] = {};
+    float seg_scale[kMaxSegments] = {};
+    int glu = 0;
+    float gate_scale = 0.0f, up_scale = 0.0f;
+};
+
+// Weight scale of 16-row group grp: its segment's scale, or dflt without segments.
+__host__ __device__ inline float group_scale(const OutForm& of, int grp, float dflt)
+{
+    if (of.nseg == 0) return dflt;
+    float s = of.seg_scale[0];
+    for (int i = 1; i < kMaxSegments; i++)
+        if (i < of.nseg && grp >= of.seg_end[i - 1]) s = of.seg_scale[i];
+    return s;
+}
+
+// SiLU(g) * u in fp32 (SiLU(z) = z / (1 + e^-z)); e^-z overflowing to infinity gives -0.
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // Internal launchers (quant.hip, gemm.hip).  Arguments are validated by the caller.
 hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
                            uint8_t* codes, float* scales, float* xh, hipStream_t stream);
@@ -32,19 +62,22 @@ hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadam
 // rows [l*M, (l+1)*M), scales[l*M ...], weights wptrs[l] (or w0 when wptrs is null) and
 // wscales[l] (or wscale0), and writes rows [l*M, (l+1)*M) of the output.
 // out_f32 != nullptr: out = (float(acc) * scale[m]) * w_scale;  else acc_i32 receives acc.
+// of: output form (segments / gate-up pairs), only with L = 1 and out_f32.
 hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bits,
                        const uint8_t* const* wptrs, const uint8_t* w0, const float* scales,
                        const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
-                       hipStream_t stream);
+                       hipStream_t stream, const OutForm& of = OutForm());
 
 // Kernel variants behind launch_gemm: M <= 16 (gemm_decode.hip) and any M (gemm.hip).
 hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
                               const uint8_t* const* wptrs, const uint8_t* w0,
                               const float* scales, const float* wscales, float wscale0,
-                              float* out_f32, int32_t* acc_i32, hipStream_t stream);
+                              float* out_f32, int32_t* acc_i32, hipStream_t stream,
+                              const OutForm& of);
 hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
                              const uint8_t* const* wptrs, const uint8_t* w0,
                              const float* scales, const float* wscales, float wscale0,
-                             float* out_f32, int32_t* acc_i32, hipStream_t stream);
+                             float* out_f32, int32_t* acc_i32, hipStream_t stream,
+                             const OutForm& of);
 
 }  // namespace bitnet

@@ -88,9 +88,10 @@ struct LargeArgs {
     const uint8_t* w0;
     const float* wscales;          // device array of L weight scales, or null (then wscale0)
     float wscale0;
-    float* out;                    // L x M x N fp32, or null
+    float* out;                    // L x M x N fp32 (M x N/2 with of.glu), or null
     int32_t* acc;                  // L x M x N int32, or null
     int M, K, N;
+    OutForm of;                    // segments / gate-up pairs (L = 1, out only)
 };
 
 // Workgroup barrier after this wave's LDS operations have completed.  Written out (rather
@@ -131,12 +132,13 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // Writes one wave's FM x FN grid of 16x16 MFMA output tiles: tile (fm, fn), lane l, register r
 // is row row0 + 16 fm + 4 (l >> 4) + r, column col0 + 16 fn + (l & 15).  With DEQ the value is
 // y = (float(acc >> SHIFT) * s_x[row]) * gamma_w, else the int32 sum acc >> SHIFT; sxf(fm)
-// gives s_x of the lane's four rows of tile fm.  Every store is issued without waiting on the
-// ones before it: an output outside M x N gets a byte offset past the buffer's range, and the
-// hardware drops it.  The caller guarantees 4 M N < 2^31.
-template <int FM, int FN, int SHIFT, bool DEQ, typename ScaleFn>
+// gives s_x of the lane's four rows of tile fm, wsf(fn) gamma_w of tile column fn.  Every
+// store is issued without waiting on the ones before it: an output outside M x N gets a byte
+// offset past the buffer's range, and the hardware drops it.  The caller guarantees
+// 4 M N < 2^31.
+template <int FM, int FN, int SHIFT, bool DEQ, typename ScaleFn, typename WScaleFn>
 __device__ __forceinline__ void store_tiles(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
-                                            int M, int N, ScaleFn sxf, float w_scale, void* obase)
+                                            int M, int N, ScaleFn sxf, WScaleFn wsf, void* obase)
 {
     const int g = lane >> 4;
     const auto ors = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 0x7FFFFFFF, 0x00020000);
@@ -153,10 +155,40 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[FM][FN], int row0, 
                 const int32_t a = acc[fm][fn][r] >> SHIFT;
                 uint32_t v;
                 if constexpr (DEQ)
-                    v = __builtin_bit_cast(uint32_t, ((float)a * sx[r]) * w_scale);
+                    v = __builtin_bit_cast(uint32_t, ((float)a * sx[r]) * wsf(fn));
                 else
                     v = (uint32_t)a;
                 const uint32_t off = (row < M && col < N) ? 4u * (uint32_t)(row * N + col) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(v, ors, (int)off, 0, 0);
+            }
+        }
+    }
+}
+
+// Gate / up pairs: tile columns 2j (gate rows) and 2j + 1 (the same up rows) of the grid above
+// give h = SiLU(gate) * up, each dequantised as in store_tiles with its own weight scale, in
+// column col0 / 2 + 16 j + (l & 15) of the M x F output (col0 a multiple of 32).
+template <int FM, int FN, int SHIFT, typename ScaleFn>
+__device__ __forceinline__ void store_tiles_glu(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
+                                                int M, int F, ScaleFn sxf, float gate_scale,
+                                                float up_scale, void* obase)
+{
+    static_assert(FN % 2 == 0, "gate / up tiles come in pairs");
+    const int g = lane >> 4;
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = row0 + 16 * fm + 4 * g + r;
+#pragma unroll
+            for (int j = 0; j < FN / 2; j++) {
+                const int col = col0 / 2 + 16 * j + (lane & 15);
+                const float gv = ((float)(acc[fm][2 * j][r] >> SHIFT) * sx[r]) * gate_scale;
+                const float uv = ((float)(acc[fm][2 * j + 1][r] >> SHIFT) * sx[r]) * up_scale;
+                const uint32_t v = __builtin_bit_cast(uint32_t, silu_mul(gv, uv));
+                const uint32_t off = (row < M && col < F) ? 4u * (uint32_t)(row * F + col) : 0x80000000u;
                 __builtin_amdgcn_raw_buffer_store_b32(v, ors, (int)off, 0, 0);
             }
         }
@@ -170,7 +202,11 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
     return ((n ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
 }
 
-template <int BITS, bool DEQ>
+// Epilogue forms, one instantiation each (the plain one carries none of the others' code):
+// one weight scale per layer; a scale per row segment; gate / up pairs.
+enum Epi { kPlain = 0, kSegments = 1, kGlu = 2 };
+
+template <int BITS, bool DEQ, int EPI>
 __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
 {
     __shared__ __align__(16) uint8_t As[2][BM * LROW];
@@ -336,12 +372,23 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
                 sxr[fm][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                     srs, 4 * (m0 + wm * 128 + 16 * fm + 4 * (lane >> 4) + r), 0, 0));
     }
-    store_tiles<8, 4, 0, DEQ>(acc, m0 + wm * 128, n0 + wn * 64, lane, M, N,
-                              [&](int fm) __attribute__((always_inline)) { return sxr[fm]; }, w_scale, obase);
+    const int col0 = n0 + wn * 64;
+    auto sxf = [&](int fm) __attribute__((always_inline)) { return sxr[fm]; };
+    if constexpr (EPI == kGlu)
+        store_tiles_glu<8, 4, 0>(acc, m0 + wm * 128, col0, lane, M, N / 2, sxf, args.of.gate_scale,
+                                 args.of.up_scale, obase);
+    else if constexpr (EPI == kSegments)
+        store_tiles<8, 4, 0, DEQ>(acc, m0 + wm * 128, col0, lane, M, N, sxf,
+                                  [&](int fn) __attribute__((always_inline)) {
+                                      return group_scale(args.of, col0 / 16 + fn, w_scale);
+                                  }, obase);
+    else
+        store_tiles<8, 4, 0, DEQ>(acc, m0 + wm * 128, col0, lane, M, N, sxf,
+                                  [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
 }
 
 
-template <bool DEQ>
+template <bool DEQ, int EPI>
 __global__ __launch_bounds__(NT4) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tern4_kernel(LargeArgs args)
 {
@@ -572,10 +619,20 @@ void gemm_tern4_kernel(LargeArgs args)
     // The codes entered the MFMAs as 16 x code, so the sums are 16 x the integer dot products.
     const float w_scale = args.wscales ? ((const_f32_ptr)(const void*)args.wscales)[layer] : args.wscale0;
     void* obase = DEQ ? (void*)(args.out + (int64_t)layer * M * N) : (void*)(args.acc + (int64_t)layer * M * N);
-    store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N,
-                              [&](int fm) __attribute__((always_inline)) {
-                                  return *(const f4*)&sxs[128 * wave + 16 * fm + 4 * g];
-                              }, w_scale, obase);
+    auto sxf = [&](int fm) __attribute__((always_inline)) {
+        return *(const f4*)&sxs[128 * wave + 16 * fm + 4 * g];
+    };
+    if constexpr (EPI == kGlu)
+        store_tiles_glu<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, M, N / 2, sxf, args.of.gate_scale,
+                                 args.of.up_scale, obase);
+    else if constexpr (EPI == kSegments)
+        store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
+                                  [&](int fn) __attribute__((always_inline)) {
+                                      return group_scale(args.of, n0 / 16 + fn, w_scale);
+                                  }, obase);
+    else
+        store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
+                                  [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
 }
 
 }  // namespace
@@ -583,7 +640,8 @@ void gemm_tern4_kernel(LargeArgs args)
 hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
                              const uint8_t* const* wptrs, const uint8_t* w0,
                              const float* scales, const float* wscales, float wscale0,
-                             float* out_f32, int32_t* acc_i32, hipStream_t stream)
+                             float* out_f32, int32_t* acc_i32, hipStream_t stream,
+                             const OutForm& of)
 {
     // Buffer ranges are 32-bit: one weight matrix, one layer's codes and one layer's output
     // stay below 2 GiB.
@@ -592,15 +650,19 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
     if (packed >= ((int64_t)1 << 31) || (int64_t)M * crow >= ((int64_t)1 << 31) ||
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
-    LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N};
+    LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N, of};
     if (bits == 4) {
         dim3 grid((N + BN4 - 1) / BN4, (M + BM4 - 1) / BM4, L);
-        if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4_kernel<true>), grid, dim3(NT4), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_tern4_kernel<false>), grid, dim3(NT4), 0, stream, a);
+        if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4_kernel<true, kSegments>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4_kernel<true, kPlain>), grid, dim3(NT4), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern4_kernel<false, kPlain>), grid, dim3(NT4), 0, stream, a);
     } else {
         dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, L);
-        if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern_kernel<8, true>), grid, dim3(NT), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_tern_kernel<8, false>), grid, dim3(NT), 0, stream, a);
+        if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kGlu>), grid, dim3(NT), 0, stream, a);
+        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kSegments>), grid, dim3(NT), 0, stream, a);
+        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kPlain>), grid, dim3(NT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern_kernel<8, false, kPlain>), grid, dim3(NT), 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -608,13 +670,13 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
 hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bits,
                        const uint8_t* const* wptrs, const uint8_t* w0, const float* scales,
                        const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
-                       hipStream_t stream)
+                       hipStream_t stream, const OutForm& of)
 {
     if (M <= 16)
         return launch_gemm_decode(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
-                                  out_f32, acc_i32, stream);
+                                  out_f32, acc_i32, stream, of);
     return launch_gemm_large(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
-                             out_f32, acc_i32, stream);
+                             out_f32, acc_i32, stream, of);
 }
 
 }  // namespace bitnet

@@ -87,9 +87,10 @@ struct DecodeArgs {
     const uint8_t* w0;
     const float* wscales;          // device array of L weight scales, or null (then wscale0)
     float wscale0;
-    float* out;                    // L x M x N fp32, or null
+    float* out;                    // L x M x N fp32 (M x N/2 with of.glu), or null
     int32_t* acc;                  // L x M x N int32, or null
     int L, M, K, N;
+    OutForm of;                    // segments / gate-up pairs (L = 1, out only)
 };
 
 // Cache policy of the weight loads and output stores: non-temporal.  Each weight byte and each
@@ -195,7 +196,12 @@ struct StreamPos {
     float ws;
 };
 
-template <int BITS, bool DEQ, int TPW>
+// Epilogue forms of the streaming kernel, one instantiation each, so that the plain one carries
+// none of the others' code inside its loop: one weight scale per layer; a scale per row
+// segment; gate / up pairs.
+enum Epi { kPlain = 0, kSegments = 1, kGlu = 2 };
+
+template <int BITS, bool DEQ, int TPW, int EPI = kPlain>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
     constexpr int WAVE_ROWS = 16 * TPW, WG_ROWS = wg_rows(TPW);
@@ -331,10 +337,37 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     };
 
     // Epilogue of an item.  MFMA 16x16 output: lane l, register r -> row 4 (l >> 4) + r,
-    // column l & 15.
+    // column l & 15.  Gate / up pairs (tiles 2j, 2j + 1) leave as SiLU(gate) * up in column
+    // (first row of the wave) / 2 + 16 j + (l & 15) of the M x N/2 output.
     auto finish = [&](const StreamPos& p, int buf) {
         const float wsc = DEQ ? sbuf[buf][16] : 0.0f;
-        const int nbase = p.c * WG_ROWS + wave * WAVE_ROWS + (lane & 15);
+        const int row0 = p.c * WG_ROWS + wave * WAVE_ROWS;
+        if constexpr (EPI == kGlu) {
+            static_assert(DEQ && TPW % 2 == 0, "gate / up pairs need the fp32 epilogue and tile pairs");
+            {
+                const int F = N / 2;
+                const auto hs = __builtin_amdgcn_make_buffer_rsrc((void*)a.out, 0, 4 * M * F, 0x00020000);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int mo = 4 * g + r;
+                    const float sx = sbuf[buf][mo];
+#pragma unroll
+                    for (int j = 0; j < TPW / 2; j++) {
+                        const int col = row0 / 2 + 16 * j + (lane & 15);
+                        uint32_t o = 4u * ((uint32_t)mo * (uint32_t)F + (uint32_t)col);
+                        o = mo < M && col < F ? o : 0x80000000u;
+                        const float gv = ((float)acc[2 * j][r] * sx) * a.of.gate_scale;
+                        const float uv = ((float)acc[2 * j + 1][r] * sx) * a.of.up_scale;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, silu_mul(gv, uv)), hs,
+                                                              (int)o, 0, kNonTemporal);
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < TPW; f++) acc[f] = v4i{0, 0, 0, 0};
+                return;
+            }
+        }
+        const int nbase = row0 + (lane & 15);
         void* obase = DEQ ? (void*)(a.out + (int64_t)p.l * M * N) : (void*)(a.acc + (int64_t)p.l * M * N);
         const auto os = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 4 * M * N, 0x00020000);
         // Buffer stores: an element outside the M x N output gets an offset past the buffer
@@ -351,7 +384,8 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
                 o = n < N ? o : 0x80000000u;
                 uint32_t v;
                 if constexpr (DEQ)
-                    v = __builtin_bit_cast(uint32_t, ((float)acc[f][r] * sx) * wsc);
+                    v = __builtin_bit_cast(uint32_t, ((float)acc[f][r] * sx) *
+                                                     (EPI == kSegments ? group_scale(a.of, row0 / 16 + f, wsc) : wsc));
                 else
                     v = (uint32_t)acc[f][r];
                 __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, kNonTemporal);
@@ -537,7 +571,7 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_splitk_kernel(DecodeArgs a)
     if constexpr (DEQ) {
         const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t)l * M), 0, 4 * M, 0x00020000);
         const float sx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * m, 0, 0));
-        const float ws = layer_scale(a.wscales, a.wscale0, l);
+        const float ws = group_scale(a.of, gi, layer_scale(a.wscales, a.wscale0, l));
         v = __builtin_bit_cast(uint32_t, ((float)sum * sx) * ws);
     } else {
         v = (uint32_t)sum;
@@ -545,17 +579,36 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_splitk_kernel(DecodeArgs a)
     __builtin_amdgcn_raw_buffer_store_b32(v, os, (int)o, 0, kNonTemporal);
 }
 
-enum class DecodeKind { Wide, Narrow, SplitK };
+enum class DecodeKind { Wide, Pairs, Narrow, SplitK };
+
+template <int BITS, bool DEQ, int EPI>
+void launch_streaming(DecodeKind kind, int grid, const DecodeArgs& a, hipStream_t stream)
+{
+    if constexpr (EPI == kGlu) {
+        if (kind == DecodeKind::Wide)
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4, EPI>), dim3(grid), dim3(DT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 2, EPI>), dim3(grid), dim3(DT), 0, stream, a);
+    } else {
+        if (kind == DecodeKind::Wide)
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4, EPI>), dim3(grid), dim3(DT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1, EPI>), dim3(grid), dim3(DT), 0, stream, a);
+    }
+}
 
 template <int BITS, bool DEQ>
 void launch_decode(DecodeKind kind, int grid, const DecodeArgs& a, hipStream_t stream)
 {
-    if (kind == DecodeKind::Wide)
-        hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 4>), dim3(grid), dim3(DT), 0, stream, a);
-    else if (kind == DecodeKind::Narrow)
-        hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1>), dim3(grid), dim3(DT), 0, stream, a);
-    else
+    if (kind == DecodeKind::SplitK)
         hipLaunchKernelGGL((gemm_decode_splitk_kernel<BITS, DEQ>), dim3(grid), dim3(DT), 0, stream, a);
+    else if constexpr (DEQ) {
+        if (a.of.glu) launch_streaming<BITS, DEQ, kGlu>(kind, grid, a, stream);
+        else if (a.of.nseg > 0) launch_streaming<BITS, DEQ, kSegments>(kind, grid, a, stream);
+        else launch_streaming<BITS, DEQ, kPlain>(kind, grid, a, stream);
+    } else {
+        launch_streaming<BITS, DEQ, kPlain>(kind, grid, a, stream);
+    }
 }
 
 }  // namespace
@@ -577,7 +630,8 @@ int device_cus()
 hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, int bits,
                               const uint8_t* const* wptrs, const uint8_t* w0,
                               const float* scales, const float* wscales, float wscale0,
-                              float* out_f32, int32_t* acc_i32, hipStream_t stream)
+                              float* out_f32, int32_t* acc_i32, hipStream_t stream,
+                              const OutForm& of)
 {
     // Buffer ranges and lane offsets are 32-bit: one weight matrix and one layer's codes must
     // stay below 2 GiB.
@@ -585,8 +639,9 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
     if (packed >= ((int64_t)1 << 31) || (int64_t)M * K >= ((int64_t)1 << 31) ||
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
-    DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N};
+    DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N, of};
     // Enough 256-row items to give every CU one: the streaming kernel with four tiles per wave.
+    // Else, for gate / up pairs, the streaming kernel with two tiles per wave (128-row items).
     // Else, when the 16-row groups fit two workgroups per CU: one workgroup per group, K split
     // over its waves.  Else the streaming kernel with one tile per wave (64-row items).
     const int cus = device_cus();
@@ -597,6 +652,11 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
     if (items4 >= cus) {
         kind = DecodeKind::Wide;
         grid = items4 < 2 * cus ? items4 : 2 * cus;
+    } else if (of.glu) {
+        // gate / up tiles must meet in one wave: two tiles per wave (128-row items)
+        kind = DecodeKind::Pairs;
+        const int items2 = L * ((N + wg_rows(2) - 1) / wg_rows(2));
+        grid = items2 < 2 * cus ? items2 : 2 * cus;
     } else if (groups <= 2 * cus) {
         kind = DecodeKind::SplitK;
         grid = groups;

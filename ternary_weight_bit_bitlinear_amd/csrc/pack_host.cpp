@@ -8,6 +8,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
+#include <new>
 
 #include "../../include/bitnet.h"
 
@@ -83,6 +84,65 @@ int bitnet_pack_weights(const float* W, int N, int K, uint8_t* packed, float* w_
             }
         }
     }
+    return BITNET_OK;
+}
+
+int bitnet_pack_weights_segments(const float* W, int S, const int* seg_n, int K, uint8_t* packed,
+                                 float* w_scales_out)
+{
+    if (W == nullptr || seg_n == nullptr || packed == nullptr || w_scales_out == nullptr)
+        return BITNET_ERR_NULL;
+    if (S <= 0 || S > BITNET_MAX_SEGMENTS) return BITNET_ERR_UNSUPPORTED;
+    int64_t rows = 0;
+    for (int s = 0; s < S; s++) {
+        if (seg_n[s] <= 0) return BITNET_ERR_SHAPE;
+        if (seg_n[s] % 16 != 0) return BITNET_ERR_UNSUPPORTED;
+        rows += seg_n[s];
+    }
+    if (rows > (int64_t)1 << 30) return BITNET_ERR_UNSUPPORTED;
+    int rc = check_nk((int)rows, K);
+    if (rc != BITNET_OK) return rc;
+    // Whole 16-row groups: segment s's packed matrix is the next run of tiles.
+    int64_t row = 0, off = 0;
+    for (int s = 0; s < S; s++) {
+        rc = bitnet_pack_weights(W + row * K, seg_n[s], K, packed + off, &w_scales_out[s]);
+        if (rc != BITNET_OK) return rc;
+        row += seg_n[s];
+        off += (int64_t)seg_n[s] / 16 * 1024 * ((K + kBlock - 1) / kBlock);
+    }
+    return BITNET_OK;
+}
+
+int bitnet_pack_gate_up(const float* W_gate, const float* W_up, int F, int K, uint8_t* packed,
+                        float* gate_scale_out, float* up_scale_out)
+{
+    if (W_gate == nullptr || W_up == nullptr || packed == nullptr || gate_scale_out == nullptr ||
+        up_scale_out == nullptr)
+        return BITNET_ERR_NULL;
+    int rc = check_nk(F, K);
+    if (rc != BITNET_OK) return rc;
+    if (F % 16 != 0 || F > (1 << 29)) return BITNET_ERR_UNSUPPORTED;
+    const int nblk = (K + kBlock - 1) / kBlock;
+    const int64_t group = (int64_t)1024 * nblk;   // bytes of one 16-row group
+    const int64_t one = (int64_t)F / 16 * group;  // bytes of one packed F x K matrix
+    // Each matrix packed on its own (its own scale), then their groups interleaved: group 2i
+    // of the result is gate group i, group 2i + 1 up group i.  The gate matrix is packed into
+    // the second half of the output (gate group i at group slot F/16 + i), the up matrix into
+    // the first half and copied aside.  Step i writes slots 2i and 2i + 1; every gate group
+    // j > i still to be moved sits at slot F/16 + j > 2i + 1, so nothing unread is overwritten.
+    uint8_t* gate = packed + one;
+    rc = bitnet_pack_weights(W_gate, F, K, gate, gate_scale_out);
+    if (rc != BITNET_OK) return rc;
+    rc = bitnet_pack_weights(W_up, F, K, packed, up_scale_out);
+    if (rc != BITNET_OK) return rc;
+    uint8_t* up = new (std::nothrow) uint8_t[one];
+    if (up == nullptr) return BITNET_ERR_UNSUPPORTED;
+    std::memcpy(up, packed, (size_t)one);
+    for (int64_t i = 0; i < F / 16; i++) {
+        std::memmove(packed + (2 * i) * group, gate + i * group, (size_t)group);
+        std::memcpy(packed + (2 * i + 1) * group, up + i * group, (size_t)group);
+    }
+    delete[] up;
     return BITNET_OK;
 }
 

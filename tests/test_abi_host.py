@@ -156,3 +156,82 @@ def test_stage_validation():
         tb.BITNET_ERR_UNSUPPORTED
     assert L.hbitlinear_gemm_dequant(FAKE, FAKE, 16384, 256, 32768, 4, FAKE, ctypes.c_float(1.0),
                                      FAKE, NUL) == tb.BITNET_ERR_UNSUPPORTED
+
+
+# --------------------------------------------- stacked and gate / up weight layouts ----
+
+def _groups(packed, K):
+    g = 1024 * ((K + 319) // 320)
+    return packed.reshape(-1, g)
+
+
+@pytest.mark.parametrize("seg_n,K", [([16, 32, 48], 640), ([4096 // 8, 1024 // 8, 1024 // 8], 1024),
+                                     ([16], 320)])
+def test_pack_segments_is_the_concatenation_of_separate_packs(seg_n, K):
+    Ws = [si.gaussian_weights(10, n, K, layer=s, std=0.01 * (s + 1)) for s, n in enumerate(seg_n)]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    parts = [oracle.pack_weights(W) for W in Ws]
+    assert packed.size == tb.bitnet_packed_bytes(sum(seg_n), K)
+    assert np.array_equal(packed, np.concatenate([p for p, _, _ in parts]))
+    assert np.array_equal(gs, np.array([g for _, g, _ in parts], np.float32))
+    # and the stacked buffer decodes to the stacked trits
+    assert np.array_equal(tb.bitnet_unpack_weights(packed, sum(seg_n), K),
+                          np.concatenate([t for _, _, t in parts]))
+
+
+@pytest.mark.parametrize("F,K", [(16, 320), (48, 1000), (256, 4096)])
+def test_pack_gate_up_interleaves_16_row_groups(F, K):
+    Wg = si.gaussian_weights(11, F, K, layer=0)
+    Wu = si.gaussian_weights(11, F, K, layer=1, std=0.05)
+    packed, gg, gu = tb.bitnet_pack_gate_up(Wg, Wu)
+    pg, og, tg = oracle.pack_weights(Wg)
+    pu, ou, tu = oracle.pack_weights(Wu)
+    assert (np.float32(gg), np.float32(gu)) == (og, ou)
+    G = _groups(packed, K)
+    assert G.shape[0] == 2 * F // 16
+    assert np.array_equal(G[0::2], _groups(pg, K))
+    assert np.array_equal(G[1::2], _groups(pu, K))
+    t = tb.bitnet_unpack_weights(packed, 2 * F, K).reshape(F // 16, 2, 16, K)
+    assert np.array_equal(t[:, 0].reshape(F, K), tg)
+    assert np.array_equal(t[:, 1].reshape(F, K), tu)
+
+
+def test_segment_and_gate_up_validation():
+    L = tb.lib()
+    n3 = (ctypes.c_int * 3)(16, 32, 16)
+    bad = (ctypes.c_int * 2)(16, 24)
+    w3 = (ctypes.c_float * 3)(1.0, 1.0, 1.0)
+    nine = (ctypes.c_int * 9)(*([16] * 9))
+    w9 = (ctypes.c_float * 9)(*([1.0] * 9))
+    f = ctypes.c_float(1.0)
+    assert L.bitnet_pack_weights_segments(NUL, 3, n3, 64, FAKE, FAKE) == tb.BITNET_ERR_NULL
+    assert L.bitnet_pack_weights_segments(FAKE, 2, bad, 64, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_pack_weights_segments(FAKE, 9, nine, 64, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_pack_weights_segments(FAKE, 0, n3, 64, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_pack_gate_up(FAKE, NUL, 16, 64, FAKE, FAKE, FAKE) == tb.BITNET_ERR_NULL
+    assert L.bitnet_pack_gate_up(FAKE, FAKE, 24, 64, FAKE, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    # forward entries: pointers, segment lists, shapes and workspace before any launch
+    assert L.hbitlinear_forward_segments(NUL, 4, 256, 3, n3, 8, 0, FAKE, FAKE, w3, FAKE, 1 << 20,
+                                         NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_segments(FAKE, 4, 256, 3, NUL, 8, 0, FAKE, FAKE, w3, FAKE, 1 << 20,
+                                         NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_segments(FAKE, 4, 256, 2, bad, 8, 0, FAKE, FAKE, w3, FAKE, 1 << 20,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_segments(FAKE, 4, 256, 9, nine, 8, 0, FAKE, FAKE, w9, FAKE, 1 << 20,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_segments(FAKE, 4, 200, 3, n3, 8, 0, FAKE, FAKE, w3, FAKE, 1 << 20,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_segments(FAKE, 4, 256, 3, n3, 8, 0, FAKE, FAKE, w3, FAKE, 16,
+                                         NUL) == tb.BITNET_ERR_WORKSPACE
+    assert L.hbitlinear_gemm_dequant_segments(FAKE, FAKE, 4, 256, 3, n3, 8, FAKE, NUL, FAKE,
+                                              NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_swiglu(FAKE, 4, 256, 24, 8, 0, FAKE, FAKE, f, f, FAKE, 1 << 20,
+                                       NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_swiglu(FAKE, 4, 256, 0, 8, 0, FAKE, FAKE, f, f, FAKE, 1 << 20,
+                                       NUL) == tb.BITNET_ERR_SHAPE
+    assert L.hbitlinear_forward_swiglu(FAKE, 4, 256, 32, 8, 1, NUL, FAKE, f, f, FAKE, 1 << 20,
+                                       NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_swiglu(FAKE, 4, 256, 32, 8, 0, FAKE, FAKE, f, f, FAKE, 16,
+                                       NUL) == tb.BITNET_ERR_WORKSPACE
+    assert L.hbitlinear_gemm_swiglu(FAKE, FAKE, 4, 256, 32, 5, FAKE, f, f, FAKE,
+                                    NUL) == tb.BITNET_ERR_UNSUPPORTED

@@ -410,3 +410,79 @@ def test_forward_graph_replays_match_eager(tb, L, M, K, N, bits, had):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i} differs from the eager output"
+
+
+# -------------------------------------------- several linears of one input; SwishGLU ----
+
+def _gpu_codes(tb, x, bits, had):
+    M, K = x.shape
+    codes, scales = tb.hbitlinear_quantize(dev(x), bits, had)
+    torch.cuda.synchronize()
+    return codes, scales, codes_to_int8(codes, M, K, bits), scales.cpu().numpy()
+
+
+# Paths (256 CUs): M <= 16 with 768 groups -> 64-row streaming items; 6 groups -> split K;
+# 65536 rows -> 256-row streaming items; M > 16 -> the INT4 / INT8 large-M kernels, with
+# segment boundaries inside a 128-row tile.
+@pytest.mark.parametrize("M,K,seg_n,bits,had", [
+    (16, 4096, [4096, 1024, 1024], 4, False),
+    (5, 1024, [16, 48, 32], 8, True),
+    (1, 256, [16384, 16384, 16384, 16384], 8, False),
+    (300, 2048, [144, 96, 64], 4, True),
+    (100, 1024, [48, 80, 16], 8, False),
+])
+def test_forward_segments_matches_oracle(tb, M, K, seg_n, bits, had):
+    say(f"  segments M={M} K={K} seg_n={seg_n} bits={bits} had={had}")
+    x = si.normal(si.seed_for(9, 1) + K + M, M * K).reshape(M, K)
+    Ws = [si.gaussian_weights(9, n, K, layer=s, std=0.01 * (s + 1)) for s, n in enumerate(seg_n)]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    ts = [oracle.unpack(p, n, K) for p, n in
+          zip(np.split(packed, np.cumsum([tb.bitnet_packed_bytes(n, K) for n in seg_n])[:-1]), seg_n)]
+    pw = dev(packed)
+    codes, scales, q, s = _gpu_codes(tb, x, bits, had)
+    y = tb.hbitlinear_gemm_dequant_segments(codes, scales, M, K, seg_n, bits, pw, gs)
+    y_full = tb.hbitlinear_forward_segments(dev(x), seg_n, bits, had, pw, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_full)
+    expect = np.concatenate([oracle.epilogue(oracle.gemm(q, t), s, g) for t, g in zip(ts, gs)], axis=1)
+    np.testing.assert_array_equal(y.cpu().numpy(), expect)
+
+
+# Paths: M <= 16 with few groups -> two tiles per wave; 65536 weight rows -> four tiles per
+# wave; M > 16 -> INT4 / INT8 large-M kernels, with F not a multiple of the tile.
+@pytest.mark.parametrize("M,K,F,bits,had", [
+    (16, 4096, 1024, 8, False),
+    (7, 1024, 208, 4, True),
+    (3, 256, 32768, 8, False),
+    (300, 2048, 208, 4, True),
+    (100, 1024, 80, 8, False),
+])
+def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
+    say(f"  swiglu M={M} K={K} F={F} bits={bits} had={had}")
+    x = si.normal(si.seed_for(9, 2) + K + M, M * K).reshape(M, K)
+    Wg = si.gaussian_weights(9, F, K, layer=10)
+    Wu = si.gaussian_weights(9, F, K, layer=11, std=0.05)
+    packed, gg, gu = tb.bitnet_pack_gate_up(Wg, Wu)
+    t = tb.bitnet_unpack_weights(packed, 2 * F, K).reshape(F // 16, 2, 16, K)
+    tg, tu = t[:, 0].reshape(F, K), t[:, 1].reshape(F, K)
+    pw = dev(packed)
+    codes, scales, q, s = _gpu_codes(tb, x, bits, had)
+    h = tb.hbitlinear_gemm_swiglu(codes, scales, M, K, F, bits, pw, gg, gu)
+    h_full = tb.hbitlinear_forward_swiglu(dev(x), F, bits, had, pw, gg, gu)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_full)
+    g_ref = oracle.epilogue(oracle.gemm(q, tg), s, np.float32(gg))
+    u_ref = oracle.epilogue(oracle.gemm(q, tu), s, np.float32(gu))
+    expect = oracle.swiglu(g_ref, u_ref)
+    got = h.cpu().numpy()
+    # fp32 SiLU (device expf, IEEE division) then a product: a few ulp from the double-rounded
+    # oracle value
+    np.testing.assert_allclose(got, expect, rtol=2e-6, atol=1e-30)
+    assert np.count_nonzero(expect) > 0.9 * expect.size
+    # end to end against the oracle's own activation stage, rows whose codes agree
+    oh = oracle.forward_swiglu(x, oracle.pack(tg), np.float32(gg), oracle.pack(tu), np.float32(gu),
+                               F, bits, had)
+    oq, _ = oracle.quantize(x, bits, had)
+    match = np.all(oq == q, axis=1)
+    assert match.mean() > 0.9
+    np.testing.assert_allclose(got[match], oh[match], rtol=2e-6, atol=1e-30)
