@@ -42,7 +42,8 @@ def parse_args():
     p.add_argument("--large-steps", type=int, default=10)
     p.add_argument("--no-large", action="store_true", help="skip the large-M workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["headline", "decode", "wo", "wdown", "block"], default=None,
+    p.add_argument("--only", choices=["headline", "decode", "wo", "wdown", "block", "block_fused"],
+                   default=None,
                    help="run one workload only (profiling); 'headline' is the grouped decode "
                         "launch alone, without the sequential and other-M decode runs")
     p.add_argument("--copy-calibration", action="store_true",
@@ -560,6 +561,107 @@ def run_large(torch, tb, si, config, steps, warmup):
     return res
 
 
+def run_block_fused(torch, tb, si, steps, warmup):
+    """The 7B-class BitNet v2 block of the block workload (same inputs and weights) with fused
+    launches: Q, K and V as one three-segment product launch; gate and up as one launch whose
+    epilogue writes SwishGLU(gate, up); Wdown (H-BitLinear) reading that output, its real input
+    in a block.  The SwishGLU glue is work the unfused block workload does not do."""
+    import numpy as np
+    wl = si.workload(5)
+    L = {l.name: l for l in wl.linears}
+    M = L["q"].M
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    up = lambda a: torch.from_numpy(a).to(dev)
+    x_qkv = up(si.activations(5, L["q"]))
+    x_wo = up(si.activations(5, L["wo"]))
+    x_ffn = up(si.activations(5, L["gate"]))
+    seg_n = [L["q"].N, L["k"].N, L["v"].N]
+    Wqkv = np.concatenate([si.weights(5, L[n]) for n in ("q", "k", "v")])
+    p_qkv, g_qkv = tb.bitnet_pack_weights_segments(Wqkv, seg_n)
+    del Wqkv
+    p_wo, g_wo = tb.bitnet_pack_weights(si.weights(5, L["wo"]))
+    p_gu, g_gate, g_up = tb.bitnet_pack_gate_up(si.weights(5, L["gate"]), si.weights(5, L["up"]))
+    p_wd, g_wd = tb.bitnet_pack_weights(si.weights(5, L["wdown"]))
+    p_qkv, p_wo, p_gu, p_wd = up(p_qkv), up(p_wo), up(p_gu), up(p_wd)
+    F = L["gate"].N
+    Kq, Kd = L["q"].K, L["wdown"].K
+
+    def stage(K):
+        return (torch.empty(tb.hbitlinear_codes_bytes(M, K, 4), dtype=torch.uint8, device=dev),
+                torch.empty(M, dtype=torch.float32, device=dev))
+    c_qkv, c_wo, c_ffn, c_wd = stage(Kq), stage(Kq), stage(Kq), stage(Kd)
+    y_qkv = torch.empty((M, sum(seg_n)), dtype=torch.float32, device=dev)
+    y_wo = torch.empty((M, L["wo"].N), dtype=torch.float32, device=dev)
+    h = torch.empty((M, F), dtype=torch.float32, device=dev)
+    y_wd = torch.empty((M, L["wdown"].N), dtype=torch.float32, device=dev)
+
+    names = ["qkv", "wo", "gate_up_swiglu", "wdown"]
+    hads = {"qkv": False, "wo": True, "gate_up_swiglu": False, "wdown": True}
+
+    def step(tq=None, tg=None):
+        def q(j, x, c):
+            if tq: tq[j].begin(stream)
+            tb.hbitlinear_quantize(x, 4, hads[names[j]], codes=c[0], scales=c[1], stream=stream)
+            if tq: tq[j].end(stream)
+
+        def g(j, fn):
+            if tg: tg[j].begin(stream)
+            fn()
+            if tg: tg[j].end(stream)
+        q(0, x_qkv, c_qkv)
+        g(0, lambda: tb.hbitlinear_gemm_dequant_segments(c_qkv[0], c_qkv[1], M, Kq, seg_n, 4, p_qkv,
+                                                         g_qkv, out=y_qkv, stream=stream))
+        q(1, x_wo, c_wo)
+        g(1, lambda: tb.hbitlinear_gemm_dequant(c_wo[0], c_wo[1], M, Kq, L["wo"].N, 4, p_wo, g_wo,
+                                                out=y_wo, stream=stream))
+        q(2, x_ffn, c_ffn)
+        g(2, lambda: tb.hbitlinear_gemm_swiglu(c_ffn[0], c_ffn[1], M, Kq, F, 4, p_gu, g_gate, g_up,
+                                               out=h, stream=stream))
+        q(3, h, c_wd)
+        g(3, lambda: tb.hbitlinear_gemm_dequant(c_wd[0], c_wd[1], M, Kd, L["wdown"].N, 4, p_wd, g_wd,
+                                                out=y_wd, stream=stream))
+
+    for _ in range(warmup):
+        step()
+    tq = [Timer(torch, steps) for _ in names]
+    tg = [Timer(torch, steps) for _ in names]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(tq, tg)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    shapes = {"qkv": (Kq, sum(seg_n), sum(seg_n)), "wo": (Kq, L["wo"].N, L["wo"].N),
+              "gate_up_swiglu": (Kq, 2 * F, F), "wdown": (Kd, L["wdown"].N, L["wdown"].N)}
+    ops = sum(2.0 * M * n * k for k, n, _o in shapes.values())
+    e2e_bytes = 0.0
+    per = {}
+    for j, name in enumerate(names):
+        k, n, n_out = shapes[name]
+        cb = M * k // 2
+        qbytes = 4 * M * k + cb + 4 * M
+        e2e_bytes += qbytes + cb + 4 * M + canonical_packed_bytes(n, k) + 4 * M * n_out
+        g_ms, q_ms = tg[j].mean_ms(), tq[j].mean_ms()
+        per[name] = dict(gemm_us=1e3 * g_ms, gemm_tops=2.0 * M * n * k / (g_ms * 1e-3) / 1e12,
+                         quant_us=1e3 * q_ms, quant_gbs=qbytes / (q_ms * 1e-3) / 1e9)
+    gemm_s = sum(t.mean_ms() for t in tg) * 1e-3
+    quant_s = sum(t.mean_ms() for t in tq) * 1e-3
+    res = dict(workload=f"bitnet_v2_7b_block_fused_int4_M{M}", M=M, ms_per_step=1e3 * dt / steps,
+               tokens_per_s=M * steps / dt, int_tops=ops * steps / dt / 1e12,
+               gemm_int_tops=ops / gemm_s / 1e12,
+               gemm_mfma_frac=ops / gemm_s / 1e12 / INT8_PEAK_TOPS,
+               end_to_end_mfma_frac=ops * steps / dt / 1e12 / INT8_PEAK_TOPS,
+               end_to_end_roofline_frac=max(e2e_bytes / (HBM_PEAK_GBS * 1e9),
+                                            ops / (INT8_PEAK_TOPS * 1e12)) / (dt / steps),
+               quant_share=quant_s / (quant_s + gemm_s), launches=per,
+               fused="qkv: one 3-segment product launch; gate/up: one launch with SwishGLU in the "
+                     "epilogue; wdown reads the SwishGLU output")
+    del x_qkv, x_wo, x_ffn, h, y_qkv, y_wo, y_wd
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -663,13 +765,16 @@ def main():
         del d
         torch.cuda.empty_cache()
 
-    if not args.no_large and args.only in (None, "wo", "wdown", "block"):
+    if not args.no_large and args.only in (None, "wo", "wdown", "block", "block_fused"):
         large = {}
-        for name, cfg in (("wo", 3), ("wdown", 4), ("block", 5)):
+        for name, cfg in (("wo", 3), ("wdown", 4), ("block", 5), ("block_fused", 5)):
             if args.only not in (None, name):
                 continue
             log(f"[bench] {name}: preparing")
-            r = run_large(torch, tb, si, cfg, args.large_steps, 2)
+            if name == "block_fused":
+                r = run_block_fused(torch, tb, si, args.large_steps, 2)
+            else:
+                r = run_large(torch, tb, si, cfg, args.large_steps, 2)
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r

@@ -142,6 +142,13 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[FM][FN], int row0, 
 {
     const int g = lane >> 4;
     const auto ors = __builtin_amdgcn_make_buffer_rsrc(obase, 0, 0x7FFFFFFF, 0x00020000);
+    // the weight scale of each tile column, formed once (the store loop below has FM * 4 * FN
+    // stores); it is the same for the whole wave, so it is held in scalar registers
+    float wsv[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+        wsv[fn] = DEQ ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsf(fn))))
+                      : 0.0f;
 #pragma unroll
     for (int fm = 0; fm < FM; fm++) {
         f4 sx = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -155,7 +162,7 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[FM][FN], int row0, 
                 const int32_t a = acc[fm][fn][r] >> SHIFT;
                 uint32_t v;
                 if constexpr (DEQ)
-                    v = __builtin_bit_cast(uint32_t, ((float)a * sx[r]) * wsf(fn));
+                    v = __builtin_bit_cast(uint32_t, ((float)a * sx[r]) * wsv[fn]);
                 else
                     v = (uint32_t)a;
                 const uint32_t off = (row < M && col < N) ? 4u * (uint32_t)(row * N + col) : 0x80000000u;
