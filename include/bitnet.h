@@ -159,8 +159,9 @@ int hbitlinear_forward_segments(const float *x, int M, int K, int S, const int *
 /* Gated feed-forward input projections with the SwishGLU glue in the product's epilogue
  * [v2 write-up: SwishGLU; reading taken: Swish with beta = 1, SiLU(z) = z / (1 + e^-z)]:
  *   g = forward(x, gate), u = forward(x, up)   (each exactly as hbitlinear_forward)
- *   h[m][f] = SiLU(g[m][f]) * u[m][f]          (fp32; SiLU with the device expf and an IEEE
- *                                               division, so within a few ulp of the exact value)
+ *   h[m][f] = SiLU(g[m][f]) * u[m][f]          (fp32 with the hardware exp2 and reciprocal:
+ *                                               within 1e-5 relative of the exact value for
+ *                                               |g| < 80)
  * packed_gate_up as bitnet_pack_gate_up; h is M x F fp32; x, h, packed_gate_up and workspace
  * (hbitlinear_workspace_bytes(M, K, act_bits)) are device pointers.  Neither g nor u is
  * written to memory.  Shape rules as hbitlinear_forward with N = 2 F, plus F % 16 == 0. */

@@ -475,9 +475,11 @@ def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
     u_ref = oracle.epilogue(oracle.gemm(q, tu), s, np.float32(gu))
     expect = oracle.swiglu(g_ref, u_ref)
     got = h.cpu().numpy()
-    # fp32 SiLU (device expf, IEEE division) then a product: a few ulp from the double-rounded
-    # oracle value
-    np.testing.assert_allclose(got, expect, rtol=2e-6, atol=1e-30)
+    # fp32 SiLU with the hardware exp2 and reciprocal, then a product: e^-g carries the rounding
+    # of g * log2(e) (relative error ~|g| * 6e-8) plus about one ulp per operation; |g| stays
+    # far below 80 here, so 1e-5 relative bounds the difference from the double-rounded oracle
+    assert np.max(np.abs(g_ref)) < 80
+    np.testing.assert_allclose(got, expect, rtol=1e-5, atol=1e-30)
     assert np.count_nonzero(expect) > 0.9 * expect.size
     # end to end against the oracle's own activation stage, rows whose codes agree
     oh = oracle.forward_swiglu(x, oracle.pack(tg), np.float32(gg), oracle.pack(tu), np.float32(gu),
@@ -485,4 +487,4 @@ def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
     oq, _ = oracle.quantize(x, bits, had)
     match = np.all(oq == q, axis=1)
     assert match.mean() > 0.9
-    np.testing.assert_allclose(got[match], oh[match], rtol=2e-6, atol=1e-30)
+    np.testing.assert_allclose(got[match], oh[match], rtol=1e-5, atol=1e-30)
