@@ -68,6 +68,10 @@ def lib():
         L.bitnet_ref_epilogue.argtypes = [P, P, F, I, I, P]; L.bitnet_ref_epilogue.restype = None
         L.bitnet_ref_forward.argtypes = [P, I, I, I, I, I, P, F, P]
         L.bitnet_ref_forward.restype = I
+        L.bitnet_ref_rms_scale.argtypes = [P, I, F]; L.bitnet_ref_rms_scale.restype = F
+        L.bitnet_ref_rmsnorm.argtypes = [P, I, I, P, F, P]; L.bitnet_ref_rmsnorm.restype = None
+        L.bitnet_ref_forward_rmsnorm.argtypes = [P, I, I, I, P, F, I, I, P, F, P]
+        L.bitnet_ref_forward_rmsnorm.restype = I
         L.bitnet_ref_forward_segments.argtypes = [P, I, I, I, P, I, I, P, P, P]
         L.bitnet_ref_forward_segments.restype = I
         L.bitnet_ref_silu.argtypes = [F]; L.bitnet_ref_silu.restype = F
@@ -250,6 +254,35 @@ def forward(x, packed, gamma_w, N: int, bits: int, use_hadamard: bool):
     y = np.empty((M, N), np.float32)
     rc = lib().bitnet_ref_forward(_p(x), M, K, N, bits, int(bool(use_hadamard)), _p(packed),
                                   float(gamma_w), _p(y))
+    if rc != 0:
+        raise ValueError("packed buffer does not decode")
+    return y
+
+
+def rms_scale(row, eps: float) -> np.float32:
+    row = _c(row, np.float32)
+    return np.float32(lib().bitnet_ref_rms_scale(_p(row), row.size, float(eps)))
+
+
+def rmsnorm(x, gain, eps: float):
+    """y = (x * r) * gain per row, r = 1 / sqrt(mean(x^2) + eps) (double sum, fp32 r)."""
+    x = _c(x, np.float32)
+    gain = _c(gain, np.float32)
+    M, K = x.shape
+    assert gain.shape == (K,)
+    y = np.empty((M, K), np.float32)
+    lib().bitnet_ref_rmsnorm(_p(x), M, K, _p(gain), float(eps), _p(y))
+    return y
+
+
+def forward_rmsnorm(x, gain, eps: float, packed, gamma_w, N: int, bits: int, use_hadamard: bool):
+    x = _c(x, np.float32)
+    gain = _c(gain, np.float32)
+    packed = _c(packed, np.uint8)
+    M, K = x.shape
+    y = np.empty((M, N), np.float32)
+    rc = lib().bitnet_ref_forward_rmsnorm(_p(x), M, K, N, _p(gain), float(eps), bits,
+                                          int(bool(use_hadamard)), _p(packed), float(gamma_w), _p(y))
     if rc != 0:
         raise ValueError("packed buffer does not decode")
     return y

@@ -329,6 +329,43 @@ int bitnet_ref_forward(const float *x, int M, int K, int N, int bits, int use_ha
 }
 
 /* ------------------------------------------------------------------------------------- */
+/* RMS normalisation of a token row before its activation stage [v2-news: LLaMA-like        */
+/* components, among them RMS normalisation; 2B4T write-up section 1.3: subln               */
+/* normalisation].  Reading taken: y[k] = (x[k] * r) * gain[k] with                          */
+/* r = 1 / sqrt(mean_k x[k]^2 + eps); eps is the caller's (the pages give none).  The sum of  */
+/* squares is taken in double (each fp32 square is exact there), r is computed in double and */
+/* rounded to fp32 once; a row whose mean square plus eps is 0 gives r = 0 (a zero row).      */
+/* ------------------------------------------------------------------------------------- */
+float bitnet_ref_rms_scale(const float *x, int K, float eps)
+{
+    double ss = 0.0;
+    for (int k = 0; k < K; k++) ss += (double)x[k] * (double)x[k];
+    const double ms = ss / (double)K + (double)eps;
+    return ms > 0.0 ? (float)(1.0 / sqrt(ms)) : 0.0f;
+}
+
+void bitnet_ref_rmsnorm(const float *x, int M, int K, const float *gain, float eps, float *y)
+{
+    for (int m = 0; m < M; m++) {
+        const float *xr = x + (int64_t)m * K;
+        const float r = bitnet_ref_rms_scale(xr, K, eps);
+        for (int k = 0; k < K; k++) y[(int64_t)m * K + k] = (xr[k] * r) * gain[k];
+    }
+}
+
+/* The forward with the norm in front: rmsnorm, then bitnet_ref_forward. */
+int bitnet_ref_forward_rmsnorm(const float *x, int M, int K, int N, const float *gain, float eps,
+                               int bits, int use_hadamard, const uint8_t *packed, float gamma_w,
+                               float *y)
+{
+    float *xn = (float *)malloc(sizeof(float) * (size_t)M * (size_t)K);
+    bitnet_ref_rmsnorm(x, M, K, gain, eps, xn);
+    int rc = bitnet_ref_forward(xn, M, K, N, bits, use_hadamard, packed, gamma_w, y);
+    free(xn);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------- */
 /* Several linears that read the same input (for instance Q, K and V of a block), each with  */
 /* its own packed weights and weight scale: y is M x (N_0 + ... + N_{S-1}), segment s in the */
 /* columns that follow segments 0 .. s-1, each exactly bitnet_ref_forward of that matrix.     */

@@ -453,3 +453,57 @@ def test_forward_swiglu_zero_gate_or_up_gives_zero():
     assert gz == 0
     assert np.all(oracle.forward_swiglu(x, pz, gz, pw, gw, F, 8, True) == 0)
     assert np.all(oracle.forward_swiglu(x, pw, gw, pz, gz, F, 8, True) == 0)
+
+
+# ------------------------------------------------------------------- RMS normalisation ----
+
+def test_rmsnorm_constant_rows_power_of_two():
+    # x = c (c a power of two), eps = 0: r = 1/|c| exactly, so y = sign(c) exactly
+    K = 512
+    ones = np.ones(K, np.float32)
+    for c in (4.0, -0.125, 1024.0):
+        y = oracle.rmsnorm(np.full((1, K), c, np.float32), ones, 0.0)
+        assert np.all(y == np.float32(math.copysign(1.0, c)))
+
+
+def test_rmsnorm_unit_rms_and_exact_power_of_two_invariance():
+    x = si.wo_activations(6, 1024)
+    ones = np.ones(1024, np.float32)
+    y = oracle.rmsnorm(x, ones, 0.0)
+    assert np.allclose(np.mean(y.astype(np.float64) ** 2, axis=1), 1.0, rtol=1e-6, atol=0)
+    for p in (-7, 5):
+        assert np.array_equal(oracle.rmsnorm(x * np.float32(2.0 ** p), ones, 0.0), y)
+
+
+def test_rmsnorm_spike_closed_form_and_eps():
+    K, j, a = 2048, 77, np.float32(-3.5)
+    x = np.zeros((1, K), np.float32); x[0, j] = a
+    g = si.normal(si.seed_for(1, 9), K, 1.0, 0.1)
+    for eps in (0.0, 1e-6, 0.25):
+        y = oracle.rmsnorm(x, g, eps)
+        r = 1.0 / math.sqrt(float(a) ** 2 / K + eps)
+        assert abs(float(y[0, j]) - float(a) * r * float(g[j])) <= 2e-7 * abs(float(a) * r * float(g[j]))
+        assert np.count_nonzero(y) == 1
+        # the fp32 scale is the double formula rounded once
+        assert oracle.rms_scale(x[0], eps) == np.float32(r)
+
+
+def test_rmsnorm_zero_rows_and_gain_factor():
+    K = 256
+    g = si.normal(si.seed_for(1, 10), K, 1.0, 0.2)
+    z = np.zeros((2, K), np.float32)
+    assert np.all(oracle.rmsnorm(z, g, 0.0) == 0) and np.all(oracle.rmsnorm(z, g, 1e-5) == 0)
+    x = si.gaussian_activations(1, 3, K)
+    # y(x, g) = y(x, 1) * g elementwise, exactly: (x r) g vs ((x r) 1) g
+    assert np.array_equal(oracle.rmsnorm(x, g, 1e-6),
+                          oracle.rmsnorm(x, np.ones(K, np.float32), 1e-6) * g)
+
+
+def test_forward_rmsnorm_is_norm_then_forward():
+    rng = np.random.default_rng(21)
+    M, K, N = 5, 1024, 48
+    x = rng.normal(0, 3, size=(M, K)).astype(np.float32)
+    g = si.normal(si.seed_for(1, 11), K, 1.0, 0.1)
+    packed, gw, t = oracle.pack_weights(si.gaussian_weights(12, N, K))
+    y = oracle.forward_rmsnorm(x, g, 1e-6, packed, gw, N, 4, True)
+    assert np.array_equal(y, oracle.forward(oracle.rmsnorm(x, g, 1e-6), packed, gw, N, 4, True))
