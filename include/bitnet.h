@@ -143,6 +143,20 @@ int hbitlinear_forward_grouped(int L, const float *x, int M, int K, int N, int a
                                const float *w_scales, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* The forward with the RMS normalisation in front folded into the activation stage's single
+ * read of x [v2 write-up: LLaMA-like components with RMS normalisation; 2B4T write-up section
+ * 1.3: subln normalisation; reading taken: per token
+ *   r = fp32(1 / sqrt(sum_k x[k]^2 / K + eps))   (the sum and r in double)
+ *   x'[k] = (x[k] * r) * gain[k]                  (fp32; a row with mean square + eps == 0
+ *                                                  gives r = 0)
+ * then exactly hbitlinear_forward on x'].  gain: K fp32 (device); eps: finite, >= 0 (the pages
+ * give none; the caller's).  K must be a power of two in [256, 16384]; other rules and the
+ * workspace as hbitlinear_forward. */
+int hbitlinear_forward_rmsnorm(const float *x, int M, int K, int N, const float *gain, float eps,
+                               int act_bits, int use_hadamard, float *out,
+                               const uint8_t *packed_w, float w_scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Several linears of one input in one call: x's activation stage runs once, then one product
  * launch covers the S stacked matrices of bitnet_pack_weights_segments:
  *   out[m][c] = forward(x, matrix s, w_scales[s])[m][c - c_s] for the columns
@@ -189,6 +203,12 @@ int hbitlinear_codes_bytes(int M, int K, int act_bits, size_t *bytes_out);
  * fp32, may be NULL) receives x_h. */
 int hbitlinear_quantize(const float *x, int M, int K, int act_bits, int use_hadamard,
                         uint8_t *codes, float *scales, float *xh_or_null, void *stream);
+
+/* The activation stage of hbitlinear_forward_rmsnorm: hbitlinear_quantize applied to the
+ * RMS-normalised rows x' (xh_or_null receives x' after the optional transform). */
+int hbitlinear_quantize_rmsnorm(const float *x, int M, int K, const float *gain, float eps,
+                                int act_bits, int use_hadamard, uint8_t *codes, float *scales,
+                                float *xh_or_null, void *stream);
 
 /* Ternary product [2B4T write-up section 1.2]: acc[m][n] = sum_k q[m][k] t[n][k], exact
  * int32.  codes as written by hbitlinear_quantize; packed_w as bitnet_pack_weights; acc is

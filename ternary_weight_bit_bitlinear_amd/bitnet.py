@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_grouped_workspace_bytes": ([I, I, I, I, PSZ], I),
             "hbitlinear_forward_grouped": ([I, P, I, I, I, I, I, P, P, P, P, SZ, P], I),
             "hbitlinear_gemm_dequant_grouped": ([P, P, I, I, I, I, I, P, P, P, P], I),
+            "hbitlinear_quantize_rmsnorm": ([P, I, I, P, F, I, I, P, P, P, P], I),
+            "hbitlinear_forward_rmsnorm": ([P, I, I, I, P, F, I, I, P, P, F, P, SZ, P], I),
             "bitnet_pack_weights_segments": ([P, I, P, I, P, P], I),
             "bitnet_pack_gate_up": ([P, P, I, I, P, P, P], I),
             "hbitlinear_forward_segments": ([P, I, I, I, P, I, I, P, P, P, P, SZ, P], I),
@@ -427,4 +429,54 @@ def hbitlinear_gemm_swiglu(codes, scales, M: int, K: int, F: int, act_bits: int,
     _check(lib().hbitlinear_gemm_swiglu(_ptr(codes), _ptr(scales), M, K, F, act_bits,
                                         _ptr(packed_gate_up), float(gate_scale), float(up_scale),
                                         _ptr(out), _stream(stream)), "hbitlinear_gemm_swiglu")
+    return out
+
+
+def hbitlinear_quantize_rmsnorm(x, gain, eps: float, act_bits: int, use_hadamard: bool, codes=None,
+                                scales=None, want_xh: bool = False, stream=None):
+    """Activation stage with the RMS norm in front -> (codes, scales[, x' after the transform])."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(gain, torch.float32, "gain")
+    M, K = x.shape
+    if gain.numel() < K:
+        raise ValueError("gain needs K entries")
+    if codes is None:
+        codes = torch.empty(hbitlinear_codes_bytes(M, K, act_bits), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    xh = torch.empty((M, K), dtype=torch.float32, device=x.device) if want_xh else None
+    _check(lib().hbitlinear_quantize_rmsnorm(_ptr(x), M, K, _ptr(gain), float(eps), act_bits,
+                                             int(bool(use_hadamard)), _ptr(codes), _ptr(scales),
+                                             _ptr(xh), _stream(stream)), "hbitlinear_quantize_rmsnorm")
+    return (codes, scales, xh) if want_xh else (codes, scales)
+
+
+def hbitlinear_forward_rmsnorm(x, gain, eps: float, N: int, act_bits: int, use_hadamard: bool,
+                               packed_w, w_scale: float, out=None, workspace=None, stream=None):
+    """out = forward(RMSNorm(x) * gain) for x (M x K fp32, device)."""
+    import torch
+    _dev_check(x, torch.float32, "x")
+    _dev_check(gain, torch.float32, "gain")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    M, K = x.shape
+    if gain.numel() < K:
+        raise ValueError("gain needs K entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev_check(out, torch.float32, "out")
+    if out.numel() < M * N:
+        raise ValueError("out is too small")
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_workspace_bytes(M, K, act_bits), dtype=torch.uint8,
+                                device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward_rmsnorm(_ptr(x), M, K, N, _ptr(gain), float(eps), act_bits,
+                                            int(bool(use_hadamard)), _ptr(out), _ptr(packed_w),
+                                            float(w_scale), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)), "hbitlinear_forward_rmsnorm")
     return out

@@ -40,6 +40,16 @@ size_t workspace_bytes(int M, int K, int bits)
     return align256(codes_bytes(M, K, bits)) + align256((size_t)M * sizeof(float));
 }
 
+// The RMS-norm front of the activation stage: a gain vector, a finite eps >= 0, and a
+// power-of-two K in [256, 16384] (the one-pass row kernel).
+int check_norm(int K, const float* gain, float eps)
+{
+    if (gain == nullptr) return BITNET_ERR_NULL;
+    if (!(eps >= 0.0f) || eps > 3.4e38f) return BITNET_ERR_UNSUPPORTED;
+    if ((K & (K - 1)) != 0 || K < 256 || K > 16384) return BITNET_ERR_UNSUPPORTED;
+    return BITNET_OK;
+}
+
 // Segments of a stacked weight (host arrays): checks them and fills the output form.
 int segment_form(int S, const int* seg_n, const float* w_scales, int* n_total, OutForm* of)
 {
@@ -116,6 +126,38 @@ int hbitlinear_quantize(const float* x, int M, int K, int act_bits, int use_hada
     if (rc != BITNET_OK) return rc;
     return status_of(launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, xh_or_null,
                                      (hipStream_t)stream));
+}
+
+int hbitlinear_quantize_rmsnorm(const float* x, int M, int K, const float* gain, float eps,
+                                int act_bits, int use_hadamard, uint8_t* codes, float* scales,
+                                float* xh_or_null, void* stream)
+{
+    if (x == nullptr || codes == nullptr || scales == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, 1, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_norm(K, gain, eps);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, xh_or_null,
+                                     (hipStream_t)stream, gain, eps));
+}
+
+int hbitlinear_forward_rmsnorm(const float* x, int M, int K, int N, const float* gain, float eps,
+                               int act_bits, int use_hadamard, float* out, const uint8_t* packed_w,
+                               float w_scale, void* workspace, size_t workspace_size, void* stream)
+{
+    if (x == nullptr || out == nullptr || packed_w == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_norm(K, gain, eps);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s, gain, eps);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 w_scale, out, nullptr, s));
 }
 
 int bitnet_ternary_gemm_i32(const uint8_t* codes, int M, int K, int N, int act_bits,

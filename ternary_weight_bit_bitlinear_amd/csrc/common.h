@@ -62,8 +62,11 @@ __device__ inline float silu_mul(float g, float u)
 }
 
 // Internal launchers (quant.hip, gemm.hip).  Arguments are validated by the caller.
+// gain != nullptr: RMS-normalise each row first (gain: K fp32, device; eps >= 0); K must then
+// be a power of two in [256, 16384].
 hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
-                           uint8_t* codes, float* scales, float* xh, hipStream_t stream);
+                           uint8_t* codes, float* scales, float* xh, hipStream_t stream,
+                           const float* gain = nullptr, float eps = 0.0f);
 
 // Ternary product over L layers of one shape (L = 1 for a single layer).  Layer l reads codes
 // rows [l*M, (l+1)*M), scales[l*M ...], weights wptrs[l] (or w0 when wptrs is null) and

@@ -188,10 +188,12 @@ __device__ __forceinline__ int quant_code(float x, float inv)
     return q;
 }
 
-template <int L, int BITS, bool HAD>
+// NORM: the row is first RMS-normalised, y[k] = (x[k] * r) * gain[k] with
+// r = fp32(1 / sqrt(sum_k x[k]^2 / K + eps)), the sum and r taken in double.
+template <int L, int BITS, bool HAD, bool NORM>
 __global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
     const float* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
-    float* __restrict__ xh, float hadamard_c)
+    float* __restrict__ xh, float hadamard_c, const float* __restrict__ gain, float eps)
 {
     using G = Geometry<L>;
     constexpr int K = G::K, T = G::T, E = G::E;
@@ -211,6 +213,32 @@ __global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
     for (int r = 0; r < E / 4; r++) {
         f4 f = __builtin_nontemporal_load(reinterpret_cast<const f4*>(xr) + r * T + t);
         v[4 * r] = f[0]; v[4 * r + 1] = f[1]; v[4 * r + 2] = f[2]; v[4 * r + 3] = f[3];
+    }
+
+    if constexpr (NORM) {
+        // Each fp32 square is exact in double, so the row sum is the same to ~K 2^-53 relative
+        // in any order: far below the fp32 rounding of r.  Waves reduce with shuffles, then in
+        // a fixed order through LDS.
+        __shared__ double rss[T / 64];
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; e++) ss += (double)v[e] * (double)v[e];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if ((t & 63) == 0) rss[t >> 6] = ss;
+        __syncthreads();
+        ss = rss[0];
+#pragma unroll
+        for (int w = 1; w < T / 64; w++) ss += rss[w];
+        const double ms = ss / (double)K + (double)eps;
+        const float rs = ms > 0.0 ? (float)(1.0 / __builtin_sqrt(ms)) : 0.0f;
+        // the gains in load layout A: the same float4 positions as the row
+#pragma unroll
+        for (int r = 0; r < E / 4; r++) {
+            const f4 gv = reinterpret_cast<const f4*>(gain)[r * T + t];
+#pragma unroll
+            for (int j = 0; j < 4; j++) v[4 * r + j] = (v[4 * r + j] * rs) * gv[j];
+        }
     }
 
     if constexpr (HAD) {
@@ -345,25 +373,29 @@ __global__ __launch_bounds__(256) void quantize_rows_generic_kernel(
 
 template <int L, int BITS, bool HAD>
 hipError_t launch_rows(const float* x, int M, uint8_t* codes, float* scales, float* xh, float c,
-                       hipStream_t s)
+                       const float* gain, float eps, hipStream_t s)
 {
-    hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD>), dim3(M), dim3(Geometry<L>::T), 0, s,
-                       x, codes, scales, xh, c);
+    if (gain != nullptr)
+        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, true>), dim3(M), dim3(Geometry<L>::T), 0,
+                           s, x, codes, scales, xh, c, gain, eps);
+    else
+        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, false>), dim3(M), dim3(Geometry<L>::T), 0,
+                           s, x, codes, scales, xh, c, gain, eps);
     return hipGetLastError();
 }
 
 template <int BITS, bool HAD>
 hipError_t dispatch_L(int L, const float* x, int M, uint8_t* codes, float* scales, float* xh,
-                      float c, hipStream_t s)
+                      float c, const float* gain, float eps, hipStream_t s)
 {
     switch (L) {
-    case 8: return launch_rows<8, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 9: return launch_rows<9, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 10: return launch_rows<10, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 11: return launch_rows<11, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 12: return launch_rows<12, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 13: return launch_rows<13, BITS, HAD>(x, M, codes, scales, xh, c, s);
-    case 14: return launch_rows<14, BITS, HAD>(x, M, codes, scales, xh, c, s);
+    case 8: return launch_rows<8, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 9: return launch_rows<9, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 10: return launch_rows<10, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 11: return launch_rows<11, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 12: return launch_rows<12, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 13: return launch_rows<13, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
+    case 14: return launch_rows<14, BITS, HAD>(x, M, codes, scales, xh, c, gain, eps, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -371,7 +403,8 @@ hipError_t dispatch_L(int L, const float* x, int M, uint8_t* codes, float* scale
 }  // namespace
 
 hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadamard,
-                           uint8_t* codes, float* scales, float* xh, hipStream_t stream)
+                           uint8_t* codes, float* scales, float* xh, hipStream_t stream,
+                           const float* gain, float eps)
 {
     int L = 0;
     while ((1 << L) < K) L++;
@@ -380,12 +413,13 @@ hipError_t launch_quantize(const float* x, int M, int K, int bits, int use_hadam
     const float c = (float)(1.0 / __builtin_sqrt((double)K));
     if (use_hadamard) {
         if (!pow2) return hipErrorInvalidValue;
-        return bits == 8 ? dispatch_L<8, true>(L, x, M, codes, scales, xh, c, stream)
-                         : dispatch_L<4, true>(L, x, M, codes, scales, xh, c, stream);
+        return bits == 8 ? dispatch_L<8, true>(L, x, M, codes, scales, xh, c, gain, eps, stream)
+                         : dispatch_L<4, true>(L, x, M, codes, scales, xh, c, gain, eps, stream);
     }
     if (pow2)
-        return bits == 8 ? dispatch_L<8, false>(L, x, M, codes, scales, xh, c, stream)
-                         : dispatch_L<4, false>(L, x, M, codes, scales, xh, c, stream);
+        return bits == 8 ? dispatch_L<8, false>(L, x, M, codes, scales, xh, c, gain, eps, stream)
+                         : dispatch_L<4, false>(L, x, M, codes, scales, xh, c, gain, eps, stream);
+    if (gain != nullptr) return hipErrorInvalidValue;   // the norm needs the one-pass row kernel
     if (bits == 8)
         hipLaunchKernelGGL(quantize_rows_generic_kernel<8>, dim3(M), dim3(256), 0, stream, x, K, codes,
                            scales, xh);

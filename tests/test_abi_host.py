@@ -235,3 +235,26 @@ def test_segment_and_gate_up_validation():
                                        NUL) == tb.BITNET_ERR_WORKSPACE
     assert L.hbitlinear_gemm_swiglu(FAKE, FAKE, 4, 256, 32, 5, FAKE, f, f, FAKE,
                                     NUL) == tb.BITNET_ERR_UNSUPPORTED
+
+
+def test_rmsnorm_validation():
+    L = tb.lib()
+    f = ctypes.c_float
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 1024, NUL, f(1e-6), 8, 0, FAKE, FAKE, NUL,
+                                         NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 1024, FAKE, f(-1.0), 8, 0, FAKE, FAKE, NUL,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 1024, FAKE, f(float("nan")), 8, 0, FAKE, FAKE,
+                                         NUL, NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 1024, FAKE, f(float("inf")), 8, 0, FAKE, FAKE,
+                                         NUL, NUL) == tb.BITNET_ERR_UNSUPPORTED
+    # the norm needs the one-pass row kernel: power-of-two K in [256, 16384], with or without
+    # the transform
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 960, FAKE, f(0.0), 8, 0, FAKE, FAKE, NUL,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_quantize_rmsnorm(FAKE, 4, 32768, FAKE, f(0.0), 8, 0, FAKE, FAKE, NUL,
+                                         NUL) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_rmsnorm(FAKE, 4, 1024, 64, FAKE, f(0.0), 8, 1, NUL, FAKE, f(1.0),
+                                        FAKE, 1 << 20, NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_rmsnorm(FAKE, 4, 1024, 64, FAKE, f(0.0), 8, 1, FAKE, FAKE, f(1.0),
+                                        FAKE, 16, NUL) == tb.BITNET_ERR_WORKSPACE

@@ -488,3 +488,37 @@ def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
     match = np.all(oq == q, axis=1)
     assert match.mean() > 0.9
     np.testing.assert_allclose(got[match], oh[match], rtol=1e-5, atol=1e-30)
+
+
+# ------------------------------------------------------------ RMS norm in the activation stage ----
+
+@pytest.mark.parametrize("M,K,bits,had,eps", [(7, 4096, 4, True, 1e-6), (33, 1024, 8, False, 0.0),
+                                              (5, 16384, 4, True, 1e-5), (3, 256, 8, True, 0.5),
+                                              (600, 4096, 4, True, 1e-6)])
+def test_rmsnorm_stage_and_forward_match_oracle(tb, M, K, bits, had, eps):
+    say(f"  rmsnorm M={M} K={K} bits={bits} had={had} eps={eps}")
+    x = si.wo_activations(M, K) * np.float32(7.0)
+    x[1] = 0.0                         # zero row: r = 0 with eps = 0, codes 0 either way
+    gain = si.normal(si.seed_for(9, 3) + K, K, 1.0, 0.1)
+    codes, scales, xh = tb.hbitlinear_quantize_rmsnorm(dev(x), dev(gain), eps, bits, had, want_xh=True)
+    torch.cuda.synchronize()
+    xn = oracle.rmsnorm(x, gain, eps)
+    oq, os_, oxh = oracle.quantize(xn, bits, had, want_xh=True)
+    gxh = xh.cpu().numpy()
+    amax = np.maximum(np.max(np.abs(oxh), axis=1, keepdims=True), 1e-30)
+    rel = float(np.max(np.abs(gxh - oxh) / amax))
+    assert rel <= 1e-5, rel
+    gq = codes_to_int8(codes, M, K, bits)
+    diff = gq.astype(np.int32) - oq.astype(np.int32)
+    assert np.count_nonzero(diff) <= 1e-4 * diff.size and np.all(np.abs(diff) <= 1)
+    assert np.allclose(scales.cpu().numpy(), os_, rtol=1e-5, atol=0)
+    assert np.all(gq[1] == 0)
+    # the forward: rows whose codes agree are bit-exact against the oracle's forward
+    N = 96
+    packed, gw = tb.bitnet_pack_weights(si.gaussian_weights(9, N, K, layer=20))
+    y = tb.hbitlinear_forward_rmsnorm(dev(x), dev(gain), eps, N, bits, had, dev(packed), gw)
+    torch.cuda.synchronize()
+    oy = oracle.forward_rmsnorm(x, gain, eps, packed, np.float32(gw), N, bits, had)
+    match = np.all(gq == oq, axis=1)
+    assert match.mean() > 0.9
+    np.testing.assert_array_equal(y.cpu().numpy()[match], oy[match])
