@@ -662,6 +662,42 @@ def run_block_fused(torch, tb, si, steps, warmup):
     return res
 
 
+def run_k1_rmsnorm(torch, tb, si, steps):
+    """The activation stage with and without the RMS norm folded in, at the large-M shapes: the
+    norm adds a reduction and a gain read but no pass over x."""
+    out = {}
+    for name, (M, K, had) in (("wo", (4096, 4096, True)), ("wdown", (8192, 16384, True)),
+                              ("block_qkv", (16384, 4096, False))):
+        x = torch.from_numpy(si.wo_activations(M, K)).cuda()
+        gain = torch.from_numpy(si.normal(si.seed_for(5, 12), K, 1.0, 0.1)).cuda()
+        codes = torch.empty(tb.hbitlinear_codes_bytes(M, K, 4), dtype=torch.uint8, device="cuda")
+        scales = torch.empty(M, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        res = {}
+        for mode in ("plain", "rmsnorm"):
+            def once():
+                if mode == "plain":
+                    tb.hbitlinear_quantize(x, 4, had, codes=codes, scales=scales, stream=stream)
+                else:
+                    tb.hbitlinear_quantize_rmsnorm(x, gain, 1e-6, 4, had, codes=codes, scales=scales,
+                                                   stream=stream)
+            for _ in range(3):
+                once()
+            t = Timer(torch, steps)
+            for _ in range(steps):
+                t.begin(stream)
+                once()
+                t.end(stream)
+            torch.cuda.synchronize()
+            nbytes = 4 * M * K + M * K // 2 + 4 * M + (4 * K if mode == "rmsnorm" else 0)
+            res[mode] = dict(us=1e3 * t.mean_ms(), gbs=nbytes / (t.mean_ms() * 1e-3) / 1e9)
+        res["M"], res["K"], res["hadamard"] = M, K, had
+        out[name] = res
+        del x
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -778,6 +814,11 @@ def main():
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r
+        if args.only in (None, "block_fused"):
+            log("[bench] activation stage with the RMS norm folded in")
+            large["k1_rmsnorm"] = run_k1_rmsnorm(torch, tb, si, 20)
+            for nm, v in large["k1_rmsnorm"].items():
+                log(f"[bench] k1 {nm}: plain {v['plain']['us']:.1f} us, rmsnorm {v['rmsnorm']['us']:.1f} us")
         if result:
             result["large_m"] = large
         else:
