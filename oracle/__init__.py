@@ -68,6 +68,9 @@ def lib():
         L.bitnet_ref_epilogue.argtypes = [P, P, F, I, I, P]; L.bitnet_ref_epilogue.restype = None
         L.bitnet_ref_forward.argtypes = [P, I, I, I, I, I, P, F, P]
         L.bitnet_ref_forward.restype = I
+        L.bitnet_ref_rotate_weights.argtypes = [P, I, I, P]; L.bitnet_ref_rotate_weights.restype = None
+        L.bitnet_ref_pack_weights_hadamard.argtypes = [P, I, I, P, P]
+        L.bitnet_ref_pack_weights_hadamard.restype = None
         L.bitnet_ref_rms_scale.argtypes = [P, I, F]; L.bitnet_ref_rms_scale.restype = F
         L.bitnet_ref_rmsnorm.argtypes = [P, I, I, P, F, P]; L.bitnet_ref_rmsnorm.restype = None
         L.bitnet_ref_forward_rmsnorm.argtypes = [P, I, I, I, P, F, I, I, P, F, P]
@@ -257,6 +260,25 @@ def forward(x, packed, gamma_w, N: int, bits: int, use_hadamard: bool):
     if rc != 0:
         raise ValueError("packed buffer does not decode")
     return y
+
+
+def rotate_weights(W):
+    """W_h = W H / sqrt(K) row by row (double, one rounding to fp32)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    Wh = np.empty((N, K), np.float32)
+    lib().bitnet_ref_rotate_weights(_p(W), N, K, _p(Wh))
+    return Wh
+
+
+def pack_weights_hadamard(W):
+    """Offline step of the weight + activation variant -> (packed uint8, gamma float32)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    out = np.empty(packed_bytes(N, K), np.uint8)
+    g = np.zeros(1, np.float32)
+    lib().bitnet_ref_pack_weights_hadamard(_p(W), N, K, _p(out), _p(g))
+    return out, np.float32(g[0])
 
 
 def rms_scale(row, eps: float) -> np.float32:

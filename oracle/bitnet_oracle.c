@@ -329,6 +329,38 @@ int bitnet_ref_forward(const float *x, int M, int K, int N, int bits, int use_ha
 }
 
 /* ------------------------------------------------------------------------------------- */
+/* Weight + activation Hadamard variant [v2-news: Hadamard rotation of weights and           */
+/* activations, or of activations only, both stabilise low-bit training (model-size table)]. */
+/* With the activations rotated, x_h = x H / sqrt(K), the weights are rotated the same way,   */
+/* W_h = W H / sqrt(K) row by row, so that x_h W_h^T = x W^T before quantisation.  Reading    */
+/* taken: the rotation is offline, in double with the same radix-2 order as the activation    */
+/* transform, multiplied by 1/sqrt(K) in double and rounded to fp32 once; then W_h is         */
+/* ternarised and packed exactly as any weight.  K must be a power of two.                    */
+/* ------------------------------------------------------------------------------------- */
+void bitnet_ref_rotate_weights(const float *W, int N, int K, float *Wh)
+{
+    double *row = (double *)malloc(sizeof(double) * (size_t)K);
+    const double c = 1.0 / sqrt((double)K);
+    for (int n = 0; n < N; n++) {
+        for (int k = 0; k < K; k++) row[k] = (double)W[(int64_t)n * K + k];
+        bitnet_ref_fwht_f64(row, K);
+        for (int k = 0; k < K; k++) Wh[(int64_t)n * K + k] = (float)(row[k] * c);
+    }
+    free(row);
+}
+
+/* rotate, ternarise, pack: the offline step of the variant */
+void bitnet_ref_pack_weights_hadamard(const float *W, int N, int K, uint8_t *packed, float *gamma_out)
+{
+    float *Wh = (float *)malloc(sizeof(float) * (size_t)N * (size_t)K);
+    int8_t *t = (int8_t *)malloc((size_t)N * (size_t)K);
+    bitnet_ref_rotate_weights(W, N, K, Wh);
+    bitnet_ref_ternarize(Wh, N, K, t, gamma_out);
+    bitnet_ref_pack(t, N, K, packed);
+    free(Wh); free(t);
+}
+
+/* ------------------------------------------------------------------------------------- */
 /* RMS normalisation of a token row before its activation stage [v2-news: LLaMA-like        */
 /* components, among them RMS normalisation; 2B4T write-up section 1.3: subln               */
 /* normalisation].  Reading taken: y[k] = (x[k] * r) * gain[k] with                          */

@@ -507,3 +507,52 @@ def test_forward_rmsnorm_is_norm_then_forward():
     packed, gw, t = oracle.pack_weights(si.gaussian_weights(12, N, K))
     y = oracle.forward_rmsnorm(x, g, 1e-6, packed, gw, N, 4, True)
     assert np.array_equal(y, oracle.forward(oracle.rmsnorm(x, g, 1e-6), packed, gw, N, 4, True))
+
+
+# ------------------------------------------------- weight + activation Hadamard variant ----
+
+def test_rotate_weights_equals_dense_sylvester_product():
+    # W H / sqrt(K) against the dense Sylvester matrix in float64 (an independent product)
+    for K in (8, 64, 256):
+        W = si.gaussian_weights(13, 5, K)
+        H = _sylvester(K).astype(np.float64)
+        ref = (W.astype(np.float64) @ H) / math.sqrt(K)
+        Wh = oracle.rotate_weights(W)
+        assert np.allclose(Wh, ref, rtol=0, atol=1e-7 * np.max(np.abs(ref)))
+        # fp32 rounding of the double result: within half an ulp of it, up to the double's error
+        assert np.all(np.abs(Wh.astype(np.float64) - ref) <= np.spacing(np.abs(ref).astype(np.float32)) * 0.5 + 1e-15)
+
+
+def test_rotate_weights_is_orthogonal_and_an_involution():
+    W = si.gaussian_weights(14, 7, 1024)
+    Wh = oracle.rotate_weights(W)
+    assert np.allclose(np.linalg.norm(Wh.astype(np.float64), axis=1),
+                       np.linalg.norm(W.astype(np.float64), axis=1), rtol=1e-6)
+    back = oracle.rotate_weights(Wh)
+    assert np.max(np.abs(back - W)) <= 4 * np.max(np.spacing(np.abs(W)))
+
+
+def test_rotated_product_preserves_x_w_before_quantisation():
+    # x_h W_h^T = x W^T: the rotation of both operands cancels (orthogonal H / sqrt(K))
+    K = 512
+    x = si.gaussian_activations(1, 4, K)
+    W = si.gaussian_weights(15, 9, K)
+    xh = oracle.hadamard(x).astype(np.float64)
+    Wh = oracle.rotate_weights(W).astype(np.float64)
+    assert np.allclose(xh @ Wh.T, x.astype(np.float64) @ W.astype(np.float64).T, rtol=1e-5, atol=1e-5)
+
+
+def test_pack_weights_hadamard_is_rotate_then_pack():
+    W = si.gaussian_weights(16, 32, 1024)
+    packed, g = oracle.pack_weights_hadamard(W)
+    p2, g2, _ = oracle.pack_weights(oracle.rotate_weights(W))
+    assert g == g2 and np.array_equal(packed, p2)
+    # a row that is a scaled Hadamard row rotates to a spike: one +-1 trit, the rest 0
+    K = 256
+    H = oracle.fwht(np.eye(K, dtype=np.float32))
+    Wr = np.zeros((16, K), np.float32)
+    for n in range(16):
+        Wr[n] = H[3 * n + 1] * np.float32(0.5)
+    t = oracle.unpack(oracle.pack_weights_hadamard(Wr)[0], 16, K)
+    for n in range(16):
+        assert np.count_nonzero(t[n]) == 1 and t[n, 3 * n + 1] == 1
