@@ -84,6 +84,16 @@ int bitnet_packed_bytes(int N, int K, size_t *bytes_out);
 int bitnet_pack_weights(const float *W_host, int N, int K, uint8_t *packed_host,
                         float *w_scale_out);
 
+/* The weight + activation Hadamard variant [v2 write-up, model-size table: rotating weights
+ * and activations, or activations only, both stabilise low-bit training]: W_host (N x K fp32,
+ * host, K a power of two in [256, 16384]) is rotated the way the activations are,
+ * W_h = W H_K / sqrt(K) row by row (radix-2 butterflies with span 1, 2, ..., K/2 in double,
+ * times 1/sqrt(K) in double, rounded to fp32 once; a host copy of W_h is made), then
+ * ternarised and packed exactly as bitnet_pack_weights.  Use with use_hadamard = 1: then
+ * x_h W_h^T = x W^T before quantisation. */
+int bitnet_pack_weights_hadamard(const float *W_host, int N, int K, uint8_t *packed_host,
+                                 float *w_scale_out);
+
 /* Most weight matrices one packed buffer can stack (bitnet_pack_weights_segments). */
 #define BITNET_MAX_SEGMENTS 8
 

@@ -13,5 +13,5 @@ from .bitnet import (  # noqa: F401
     hbitlinear_grouped_workspace_bytes, hbitlinear_quantize, hbitlinear_workspace_bytes, lib,
     bitnet_pack_gate_up, bitnet_pack_weights_segments, hbitlinear_forward_segments,
     hbitlinear_forward_swiglu, hbitlinear_gemm_dequant_segments, hbitlinear_gemm_swiglu,
-    hbitlinear_forward_rmsnorm, hbitlinear_quantize_rmsnorm,
+    hbitlinear_forward_rmsnorm, hbitlinear_quantize_rmsnorm, bitnet_pack_weights_hadamard,
 )

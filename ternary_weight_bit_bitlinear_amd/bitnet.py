@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_gemm_dequant_grouped": ([P, P, I, I, I, I, I, P, P, P, P], I),
             "hbitlinear_quantize_rmsnorm": ([P, I, I, P, F, I, I, P, P, P, P], I),
             "hbitlinear_forward_rmsnorm": ([P, I, I, I, P, F, I, I, P, P, F, P, SZ, P], I),
+            "bitnet_pack_weights_hadamard": ([P, I, I, P, P], I),
             "bitnet_pack_weights_segments": ([P, I, P, I, P, P], I),
             "bitnet_pack_gate_up": ([P, P, I, I, P, P, P], I),
             "hbitlinear_forward_segments": ([P, I, I, I, P, I, I, P, P, P, P, SZ, P], I),
@@ -147,6 +148,18 @@ def bitnet_pack_weights(W):
     g = ctypes.c_float(0.0)
     _check(lib().bitnet_pack_weights(_ptr(W), N, K, _ptr(packed), ctypes.byref(g)),
            "bitnet_pack_weights")
+    return packed, float(g.value)
+
+
+def bitnet_pack_weights_hadamard(W):
+    """Rotate an N x K fp32 host matrix by H_K / sqrt(K) (row by row), then ternarise and pack
+    -> (packed uint8, w_scale float).  Pair with use_hadamard=True in the forward."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    packed = np.empty(bitnet_packed_bytes(N, K), np.uint8)
+    g = ctypes.c_float(0.0)
+    _check(lib().bitnet_pack_weights_hadamard(_ptr(W), N, K, _ptr(packed), ctypes.byref(g)),
+           "bitnet_pack_weights_hadamard")
     return packed, float(g.value)
 
 

@@ -87,6 +87,39 @@ int bitnet_pack_weights(const float* W, int N, int K, uint8_t* packed, float* w_
     return BITNET_OK;
 }
 
+int bitnet_pack_weights_hadamard(const float* W, int N, int K, uint8_t* packed, float* w_scale_out)
+{
+    if (W == nullptr || packed == nullptr || w_scale_out == nullptr) return BITNET_ERR_NULL;
+    int rc = check_nk(N, K);
+    if (rc != BITNET_OK) return rc;
+    if ((K & (K - 1)) != 0 || K < 256 || K > 16384) return BITNET_ERR_UNSUPPORTED;
+    // W_h = W H / sqrt(K) row by row: radix-2 butterflies with span 1, 2, ..., K/2 in double,
+    // one multiply by 1/sqrt(K) in double, one rounding to fp32.
+    float* Wh = new (std::nothrow) float[(size_t)N * (size_t)K];
+    double* row = new (std::nothrow) double[(size_t)K];
+    if (Wh == nullptr || row == nullptr) {
+        delete[] Wh;
+        delete[] row;
+        return BITNET_ERR_UNSUPPORTED;
+    }
+    const double c = 1.0 / std::sqrt((double)K);
+    for (int n = 0; n < N; n++) {
+        for (int k = 0; k < K; k++) row[k] = (double)W[(int64_t)n * K + k];
+        for (int h = 1; h < K; h *= 2)
+            for (int base = 0; base < K; base += 2 * h)
+                for (int j = base; j < base + h; j++) {
+                    const double a = row[j], b = row[j + h];
+                    row[j] = a + b;
+                    row[j + h] = a - b;
+                }
+        for (int k = 0; k < K; k++) Wh[(int64_t)n * K + k] = (float)(row[k] * c);
+    }
+    rc = bitnet_pack_weights(Wh, N, K, packed, w_scale_out);
+    delete[] Wh;
+    delete[] row;
+    return rc;
+}
+
 int bitnet_pack_weights_segments(const float* W, int S, const int* seg_n, int K, uint8_t* packed,
                                  float* w_scales_out)
 {

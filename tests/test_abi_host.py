@@ -258,3 +258,20 @@ def test_rmsnorm_validation():
                                         FAKE, 1 << 20, NUL) == tb.BITNET_ERR_NULL
     assert L.hbitlinear_forward_rmsnorm(FAKE, 4, 1024, 64, FAKE, f(0.0), 8, 1, FAKE, FAKE, f(1.0),
                                         FAKE, 16, NUL) == tb.BITNET_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (33, 1024), (8, 4096)])
+def test_pack_weights_hadamard_matches_oracle_bytes(N, K):
+    W = si.gaussian_weights(17, N, K)
+    packed, g = tb.bitnet_pack_weights_hadamard(W)
+    opacked, og = oracle.pack_weights_hadamard(W)
+    assert np.float32(g) == og
+    assert np.array_equal(packed, opacked)
+
+
+def test_pack_weights_hadamard_validation():
+    L = tb.lib()
+    assert L.bitnet_pack_weights_hadamard(NUL, 4, 256, FAKE, FAKE) == tb.BITNET_ERR_NULL
+    assert L.bitnet_pack_weights_hadamard(FAKE, 4, 320, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_pack_weights_hadamard(FAKE, 4, 128, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
+    assert L.bitnet_pack_weights_hadamard(FAKE, 0, 256, FAKE, FAKE) == tb.BITNET_ERR_SHAPE
