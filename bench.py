@@ -789,7 +789,7 @@ def main():
             "int_tops": r["int_tops"],
             "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gemm_decode_kernel<8,true,4>", "launch_us": r["gemm_us"],
+                         "kernel": "gemm_decode_kernel<8,true,4,0>", "launch_us": r["gemm_us"],
                          "launch_us_median": r["gemm_us_median"],
                          "algorithmic_bytes_per_launch": r["gemm_bytes"]},
             "quant_kernel_us": r["quant_us"],
