@@ -430,6 +430,8 @@ def _gpu_codes(tb, x, bits, had):
     (1, 256, [16384, 16384, 16384, 16384], 8, False),
     (300, 2048, [144, 96, 64], 4, True),
     (100, 1024, [48, 80, 16], 8, False),
+    (17, 512, [16, 32, 16, 48, 16, 64, 16, 32], 4, True),   # eight segments, M just above 16
+    (16, 256, [16] * 8, 8, False),                            # eight one-group segments, split K
 ])
 def test_forward_segments_matches_oracle(tb, M, K, seg_n, bits, had):
     say(f"  segments M={M} K={K} seg_n={seg_n} bits={bits} had={had}")
@@ -456,6 +458,8 @@ def test_forward_segments_matches_oracle(tb, M, K, seg_n, bits, had):
     (3, 256, 32768, 8, False),
     (300, 2048, 208, 4, True),
     (100, 1024, 80, 8, False),
+    (17, 256, 16, 4, True),      # one gate / up pair, M just above 16 (large-M kernel)
+    (1, 256, 16, 8, False),      # one pair at decode shape
 ])
 def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
     say(f"  swiglu M={M} K={K} F={F} bits={bits} had={had}")
