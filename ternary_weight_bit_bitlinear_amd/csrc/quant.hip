@@ -32,6 +32,15 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // per thread (more waves per row) hide more of the load latency; 16 per thread measured slower
 // (one more LDS exchange), 64 per thread slower at K >= 4096.
 __host__ __device__ constexpr int threads_for(int L) { return L >= 12 ? (1 << (L - 5)) : 64; }
+
+// Without the transform there are no exchanges, so the thread count only sets how many waves
+// share a row: kPlainE elements per thread, 64 to 1024 threads.  16 measured 3-4 % faster than
+// 32 at 16384 rows of 4096 and 8192, and the same at 2048 rows (8 and 64 no better).
+constexpr int kPlainE = 16;
+__host__ __device__ constexpr int threads_plain(int L)
+{
+    return (1 << L) / kPlainE < 64 ? 64 : ((1 << L) / kPlainE > 1024 ? 1024 : (1 << L) / kPlainE);
+}
 __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v >> 1); }
 
 // Deposit the low bits of v into the set bits of mask, lowest first.
@@ -100,10 +109,10 @@ __device__ __forceinline__ void butterflies(float (&v)[E])
     }
 }
 
-template <int L>
+template <int L, bool HAD = true>
 struct Geometry {
     static constexpr int K = 1 << L;
-    static constexpr int T = threads_for(L);
+    static constexpr int T = HAD ? threads_for(L) : threads_plain(L);
     static constexpr int LT = ilog2c(T);
     static constexpr int LE = L - LT;
     static constexpr int E = 1 << LE;
@@ -173,7 +182,7 @@ __device__ __forceinline__ void transform_groups(float* lds, uint32_t t,
 template <int L, bool HAD>
 __device__ __forceinline__ constexpr uint32_t final_mask()
 {
-    using G = Geometry<L>;
+    using G = Geometry<L, HAD>;
     return HAD ? group_mask(L, G::LE, G::G - 1) : group_mask(L, G::LE, 0);
 }
 
@@ -191,11 +200,11 @@ __device__ __forceinline__ int quant_code(float x, float inv)
 // NORM: the row is first RMS-normalised, y[k] = (x[k] * r) * gain[k] with
 // r = fp32(1 / sqrt(sum_k x[k]^2 / K + eps)), the sum and r taken in double.
 template <int L, int BITS, bool HAD, bool NORM>
-__global__ __launch_bounds__(Geometry<L>::T) void quantize_rows_kernel(
+__global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
     const float* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
     float* __restrict__ xh, float hadamard_c, const float* __restrict__ gain, float eps)
 {
-    using G = Geometry<L>;
+    using G = Geometry<L, HAD>;
     constexpr int K = G::K, T = G::T, E = G::E;
     constexpr int QP = (1 << (BITS - 1)) - 1;
     // With the transform: the row for the exchanges, then the code bytes; the reduction slots
@@ -376,10 +385,10 @@ hipError_t launch_rows(const float* x, int M, uint8_t* codes, float* scales, flo
                        const float* gain, float eps, hipStream_t s)
 {
     if (gain != nullptr)
-        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, true>), dim3(M), dim3(Geometry<L>::T), 0,
+        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, true>), dim3(M), dim3(Geometry<L, HAD>::T), 0,
                            s, x, codes, scales, xh, c, gain, eps);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, false>), dim3(M), dim3(Geometry<L>::T), 0,
+        hipLaunchKernelGGL((quantize_rows_kernel<L, BITS, HAD, false>), dim3(M), dim3(Geometry<L, HAD>::T), 0,
                            s, x, codes, scales, xh, c, gain, eps);
     return hipGetLastError();
 }
