@@ -367,6 +367,43 @@ def test_decode_paths_match_oracle(tb, L, M, K, N, bits):
         np.testing.assert_array_equal(yh[l], oy, err_msg=f"layer {l}")
 
 
+# The decode workload at full size, built and launched as the benchmark does: 128 distinct
+# packed 4096 x 4096 weight buffers (copies of four seeded matrices), one activation-stage
+# launch over all 128 M rows, one grouped product launch.  Every code and scale against the
+# oracle; the outputs of sampled layers (all rows, all columns) against the oracle's product
+# and epilogue; the one-layer product launch (the layer-by-layer decode) on the same codes
+# equal to the grouped result.
+@pytest.mark.parametrize("M", [16, 4, 1])
+def test_decode_workload_full_size(tb, M):
+    L, K, N, unique = 128, 4096, 4096, 4
+    say(f"  decode workload L={L} M={M} K=N={K}")
+    packs, gs, ts = [], [], []
+    for u in range(unique):
+        packed, g = tb.bitnet_pack_weights(si.gaussian_weights(2, N, K, layer=u))
+        packs.append(dev(packed)); gs.append(g); ts.append(oracle.unpack(packed, N, K))
+    ws = [packs[l % unique].clone() for l in range(L)]
+    ptrs = torch.tensor([w.data_ptr() for w in ws], dtype=torch.int64, device="cuda")
+    wsc = torch.tensor([gs[l % unique] for l in range(L)], dtype=torch.float32, device="cuda")
+    x = si.normal(si.seed_for(2, 0), L * M * K).reshape(L * M, K)
+    codes, scales = tb.hbitlinear_quantize(dev(x), 8, False)
+    y = tb.hbitlinear_gemm_dequant_grouped(codes, scales, L, M, K, N, 8, ptrs, wsc)
+    torch.cuda.synchronize()
+    gq = codes_to_int8(codes, L * M, K, 8)
+    gsx = scales.cpu().numpy()
+    oq, osx = oracle.quantize(x, 8, False)
+    np.testing.assert_array_equal(gq, oq)
+    np.testing.assert_array_equal(gsx, osx)
+    yh = y.cpu().numpy()
+    for l in (0, 1, 2, 3, 66, L - 1):
+        r = slice(l * M, (l + 1) * M)
+        oy = oracle.epilogue(oracle.gemm(oq[r], ts[l % unique]), osx[r], np.float32(gs[l % unique]))
+        np.testing.assert_array_equal(yh[l], oy, err_msg=f"layer {l}")
+        y1 = tb.hbitlinear_gemm_dequant(codes[l * M * K:(l + 1) * M * K], scales[r], M, K, N, 8,
+                                        ws[l], gs[l % unique])
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y[l]), f"layer {l}: one-layer launch differs from the grouped one"
+
+
 # -------------------------------------------------------------------- graph capture ----
 
 @pytest.mark.parametrize("L,M,K,N,bits,had", [(4, 16, 4096, 512, 8, False), (1, 600, 4096, 384, 4, True)])
