@@ -225,6 +225,12 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
     }
 
     if constexpr (NORM) {
+        // The gains in load layout A (the same float4 positions as the row), requested with
+        // the row: loaded after the barrier below (a memory fence), they would cost each row
+        // one more round trip.
+        f4 gv[E / 4];
+#pragma unroll
+        for (int r = 0; r < E / 4; r++) gv[r] = reinterpret_cast<const f4*>(gain)[r * T + t];
         // Each fp32 square is exact in double, so the row sum is the same to ~K 2^-53 relative
         // in any order: far below the fp32 rounding of r.  Waves reduce with shuffles, then in
         // a fixed order through LDS.
@@ -241,13 +247,10 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
         for (int w = 1; w < T / 64; w++) ss += rss[w];
         const double ms = ss / (double)K + (double)eps;
         const float rs = ms > 0.0 ? (float)(1.0 / __builtin_sqrt(ms)) : 0.0f;
-        // the gains in load layout A: the same float4 positions as the row
 #pragma unroll
-        for (int r = 0; r < E / 4; r++) {
-            const f4 gv = reinterpret_cast<const f4*>(gain)[r * T + t];
+        for (int r = 0; r < E / 4; r++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) v[4 * r + j] = (v[4 * r + j] * rs) * gv[j];
-        }
+            for (int j = 0; j < 4; j++) v[4 * r + j] = (v[4 * r + j] * rs) * gv[r][j];
     }
 
     if constexpr (HAD) {
