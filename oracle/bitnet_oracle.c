@@ -23,7 +23,10 @@
  *               BitLinear replaces nn.Linear.
  *
  * Where the pages are silent the plainest reading is taken; each such reading is noted at
- * the function that makes it.  Floating point follows the precision the layer computes in
+ * the function that makes it.  Every function is pinned by the tests to values the pages or
+ * the mathematics fix, except one choice: the rounding mode of the quantisers (round half to
+ * even) is a reading no page fixes -- parity unpinned for that choice; the kernels make the
+ * same one, so parity holds by construction.  Floating point follows the precision the layer computes in
  * (fp32 activations and scales; the weight mean is accumulated in double).  Build with
  * -O2 -ffp-contract=off and no fast-math so that every fp32 operation is one IEEE rounding.
  *
