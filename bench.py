@@ -762,7 +762,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path.", flush=True)
+              "the library runs the layer on one GPU and has no multi-GPU path.", flush=True)
         sys.exit(2)
     if args.summarize_counters:
         return summarize_counters(args)
