@@ -300,21 +300,21 @@ def cpu_baseline_decode(si, oracle, d, tb, min_seconds=10.0, max_seconds=30.0):
                        f"product + epilogue per layer), {dt:.1f} s")
 
 
-def cpu_baseline_large(si, oracle, config, seconds=3.0, chunk=16):
-    """The oracle forward of every linear of a large-M workload on its first token rows
-    (seeded, as the GPU runs them), `chunk` rows at a time per linear until `seconds` have
-    passed: tokens/s for the whole workload (a token goes through every linear)."""
+def cpu_baseline_large(si, oracle, config, rows_max=256, chunk=16):
+    """The oracle forward of every linear of a large-M workload on its first `rows_max` token
+    rows (seeded, as the GPU runs them), `chunk` rows at a time per linear: tokens/s for the
+    whole workload (a token goes through every linear)."""
     M_full = si.workload(config).linears[0].M
     # the seeded generators are counter-based and row-major: the first rows of the workload are
     # the workload built with that many rows
-    wl = si.workload(config, M=min(M_full, 256))
+    wl = si.workload(config, M=min(M_full, rows_max))
     lins = []
     for lin in wl.linears:
         x = si.activations(config, lin)
         packed, g, _t = oracle.pack_weights(si.weights(config, lin))
         lins.append((lin, x, packed, g))
     rows, t_total = 0, 0.0
-    while t_total < seconds and rows + chunk <= wl.linears[0].M:
+    while rows + chunk <= wl.linears[0].M:
         t0 = time.perf_counter()
         for lin, x, packed, g in lins:
             oracle.forward(x[rows:rows + chunk], packed, g, lin.N, lin.act_bits, lin.use_hadamard)
@@ -879,6 +879,17 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg)
                     log(f"[bench] {name}: cpu oracle {r['cpu_baseline']['value']:.4g} tokens/s "
                         f"({r['cpu_baseline']['sample']})")
+                    if cfg == 3:
+                        # the same oracle on one host thread, as context
+                        nthr = oracle.num_threads()
+                        oracle.set_num_threads(1)
+                        try:
+                            r["cpu_baseline_1thread"] = cpu_baseline_large(si, oracle, cfg, rows_max=32)
+                        finally:
+                            oracle.set_num_threads(nthr)
+                        log(f"[bench] {name}: cpu oracle, one thread, "
+                            f"{r['cpu_baseline_1thread']['value']:.4g} tokens/s "
+                            f"({r['cpu_baseline_1thread']['sample']})")
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r
