@@ -19,8 +19,8 @@
 //                  fully coalesced); its register bits are {0, 1} and the top LE-2 bits.
 //   group p >= 1:  register bits are the next LE not-yet-transformed index bits, padded with
 //                  the lowest bits when fewer remain; the other bits index the thread.
-// LDS addresses are XOR-swizzled, addr(k) = k ^ (((k >> 8) & 7) << 2): it keeps 16-byte
-// chunks whole and spreads the strided accesses of the middle group over the banks.
+// LDS addresses are XOR-swizzled (swz below): 16-byte chunks stay whole and the strided
+// accesses of the middle groups spread over the banks.
 #include "common.h"
 
 namespace bitnet {
@@ -73,7 +73,17 @@ __host__ __device__ constexpr uint32_t group_mask(int L, int LE, int p)
 
 __host__ __device__ constexpr int num_groups(int L, int LE) { return 1 + (L - 2 + LE - 1) / LE; }
 
-__device__ __forceinline__ uint32_t swz(uint32_t k) { return k ^ (((k >> 8) & 7u) << 2); }
+// LDS index of element k: index bits 2.. XOR-ed with higher bits, so that 16-byte chunks stay
+// whole and the strided accesses of the exchanges spread over the banks (32 consecutive lanes
+// are served together).  For K >= 8192 bits 7..10 go into bits 2..5: with bits 8..10 only,
+// two lanes that differ in bit 7 of k meet in one bank (3-6 % slower there; smaller K measured
+// no different or faster with the narrower form).  Either form is its own inverse on [0, K).
+template <int L>
+__device__ __forceinline__ uint32_t swz(uint32_t k)
+{
+    if constexpr (L >= 13) return k ^ (((k >> 7) & 15u) << 2);
+    else return k ^ (((k >> 8) & 7u) << 2);
+}
 
 // Position of index bit b among the register bits of MASK.
 __host__ __device__ constexpr int regpos(uint32_t mask, int b)
@@ -134,11 +144,11 @@ __device__ __forceinline__ void store_layout(float* lds, uint32_t t, const float
 #pragma unroll
         for (int e = 0; e < E; e += 4) {
             uint32_t k = tb | pdep((uint32_t)e, MASK);
-            *reinterpret_cast<float4*>(lds + swz(k)) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+            *reinterpret_cast<float4*>(lds + swz<L>(k)) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < E; e++) lds[swz(tb | pdep((uint32_t)e, MASK))] = v[e];
+        for (int e = 0; e < E; e++) lds[swz<L>(tb | pdep((uint32_t)e, MASK))] = v[e];
     }
 }
 
@@ -150,12 +160,12 @@ __device__ __forceinline__ void load_layout(const float* lds, uint32_t t, float 
 #pragma unroll
         for (int e = 0; e < E; e += 4) {
             uint32_t k = tb | pdep((uint32_t)e, MASK);
-            float4 f = *reinterpret_cast<const float4*>(lds + swz(k));
+            float4 f = *reinterpret_cast<const float4*>(lds + swz<L>(k));
             v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < E; e++) v[e] = lds[swz(tb | pdep((uint32_t)e, MASK))];
+        for (int e = 0; e < E; e++) v[e] = lds[swz<L>(tb | pdep((uint32_t)e, MASK))];
     }
 }
 
