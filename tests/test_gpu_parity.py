@@ -252,6 +252,19 @@ def test_forward_ragged_shapes(tb, M, N, K, bits, had):
     check_forward(tb, lin, x, W, np.arange(M), f"ragged M={M} N={N} K={K} b={bits} h={had}")
 
 
+# The widest rows the library takes (K = 65536, and 65472, the widest that is not a power of
+# two): the activation stage's two-pass kernel, 205 packed blocks per row, int32 sums up to
+# 2^23; decode shapes (split K and streaming) and both large-M kernels.
+@pytest.mark.parametrize("M,N,K,bits", [(5, 200, 65536, 8), (16, 40, 65536, 4), (40, 200, 65536, 4),
+                                        (33, 130, 65472, 8), (7, 48, 65472, 4)])
+def test_forward_widest_rows(tb, M, N, K, bits):
+    x = si.normal(si.seed_for(6, 1) + M + K, M * K).reshape(M, K)
+    x[M - 1, ::3] *= 40.0                       # one row with a few large channels
+    W = si.gaussian_weights(6, N, K, layer=1)
+    lin = si.Linear("widest", M, K, N, bits, False, "x")
+    check_forward(tb, lin, x, W, np.arange(M), f"widest M={M} N={N} K={K} b={bits}")
+
+
 def test_forward_zero_input_gives_zero(tb):
     M, N, K = 4, 64, 4096
     W = si.gaussian_weights(7, N, K)
