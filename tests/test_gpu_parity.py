@@ -274,6 +274,31 @@ def test_forward_zero_input_gives_zero(tb):
     assert not np.any(y.cpu().numpy())
 
 
+# Degenerate weights: an all-zero matrix (gamma_w = 0, every trit 0: every byte the code of
+# digits 1,1,1,1,1 = 121, every output 0) and constant matrices (every trit +1 or -1: each
+# output is +-the row's code sum times s_x gamma_w), on the decode and large-M paths.
+@pytest.mark.parametrize("M", [1, 16, 300])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("wval", [0.0, 0.37, -2.5])
+def test_forward_degenerate_weights(tb, M, bits, wval):
+    N, K = 96, 1024
+    W = np.full((N, K), wval, np.float32)
+    packed, g = tb.bitnet_pack_weights(W)
+    if wval == 0.0:
+        assert g == 0.0
+        t = oracle.unpack(packed, N, K)
+        assert not np.any(t)
+    else:
+        assert np.float32(g) == np.float32(abs(wval))
+    x = si.normal(si.seed_for(7, 3) + M + bits, M * K).reshape(M, K)
+    lin = si.Linear("degenerate", M, K, N, bits, True, "x")
+    check_forward(tb, lin, x, W, np.arange(M), f"degenerate W={wval} M={M} b={bits}")
+    if wval == 0.0:
+        y = tb.hbitlinear_forward(dev(x), N, bits, True, dev(packed), g)
+        torch.cuda.synchronize()
+        assert not np.any(y.cpu().numpy())
+
+
 def test_forward_is_deterministic_and_stream_safe(tb):
     lin, x, W = linear_inputs(3, 0, 512)
     packed, g = tb.bitnet_pack_weights(W)
