@@ -569,6 +569,63 @@ def test_forward_swiglu_matches_oracle(tb, M, K, F, bits, had):
     np.testing.assert_allclose(got[match], oh[match], rtol=1e-5, atol=1e-30)
 
 
+# The fused launches of the 7B block at full size (M = 16384), on the block workload's inputs
+# and weights and launched as the benchmark does: Q, K and V as one three-segment product
+# launch; gate and up as one launch with the SwishGLU glue.  Sampled rows against the oracle:
+# codes and scales identical, each segment bit-exact, the glue within 1e-5 relative.
+def test_fused_block_full_size(tb):
+    wl = si.workload(5)
+    L = {l.name: l for l in wl.linears}
+    M, K = L["q"].M, L["q"].K
+    rows = sample_rows(M, 12, 55)
+    say(f"  fused block M={M} K={K}, rows {rows.tolist()}")
+
+    def stage(x):
+        codes, scales = tb.hbitlinear_quantize(dev(x), 4, False)
+        oq, osx = oracle.quantize(x[rows], 4, False)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes_to_int8(codes, M, K, 4)[rows], oq)
+        np.testing.assert_array_equal(scales.cpu().numpy()[rows], osx)
+        return codes, scales, oq, osx
+
+    # Q, K, V: one launch over the stacked matrices, a gamma_w per segment
+    x = si.activations(5, L["q"])
+    seg_n = [L[n].N for n in ("q", "k", "v")]
+    Ws = [si.weights(5, L[n]) for n in ("q", "k", "v")]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    codes, scales, oq, osx = stage(x)
+    y = tb.hbitlinear_gemm_dequant_segments(codes, scales, M, K, seg_n, 4, dev(packed), gs)
+    torch.cuda.synchronize()
+    gy = y.cpu().numpy()[rows]
+    del y, codes, scales, x
+    c0 = 0
+    for s, W in enumerate(Ws):
+        _, og, t = oracle.pack_weights(W)
+        assert np.float32(gs[s]) == og
+        oy = oracle.epilogue(oracle.gemm(oq, t), osx, og)
+        np.testing.assert_array_equal(gy[:, c0:c0 + seg_n[s]], oy, err_msg=f"segment {s}")
+        c0 += seg_n[s]
+    del Ws
+
+    # gate and up with SwishGLU in the epilogue
+    x = si.activations(5, L["gate"])
+    F = L["gate"].N
+    Wg, Wu = si.weights(5, L["gate"]), si.weights(5, L["up"])
+    packed, gg, gu = tb.bitnet_pack_gate_up(Wg, Wu)
+    codes, scales, oq, osx = stage(x)
+    h = tb.hbitlinear_gemm_swiglu(codes, scales, M, K, F, 4, dev(packed), gg, gu)
+    torch.cuda.synchronize()
+    gh = h.cpu().numpy()[rows]
+    del h, codes, scales, x
+    _, ogg, tg = oracle.pack_weights(Wg)
+    _, ogu, tu = oracle.pack_weights(Wu)
+    assert np.float32(gg) == ogg and np.float32(gu) == ogu
+    g_ref = oracle.epilogue(oracle.gemm(oq, tg), osx, ogg)
+    u_ref = oracle.epilogue(oracle.gemm(oq, tu), osx, ogu)
+    assert np.max(np.abs(g_ref)) < 80
+    np.testing.assert_allclose(gh, oracle.swiglu(g_ref, u_ref), rtol=1e-5, atol=1e-30)
+
+
 # ------------------------------------------------------------ RMS norm in the activation stage ----
 
 @pytest.mark.parametrize("M,K,bits,had,eps", [(7, 4096, 4, True, 1e-6), (33, 1024, 8, False, 0.0),
