@@ -660,6 +660,25 @@ def test_rmsnorm_stage_and_forward_match_oracle(tb, M, K, bits, had, eps):
     np.testing.assert_array_equal(y.cpu().numpy()[match], oy[match])
 
 
+# The activation stage with the norm at the three full sizes the benchmark times (its inputs:
+# Wo-like activations, gains N(1, 0.1), eps 1e-6, INT4), sampled rows against the oracle.
+@pytest.mark.parametrize("M,K,had", [(4096, 4096, True), (8192, 16384, True), (16384, 4096, False)])
+def test_rmsnorm_stage_full_size(tb, M, K, had):
+    x = si.wo_activations(M, K)
+    gain = si.normal(si.seed_for(5, 12), K, 1.0, 0.1)
+    rows = sample_rows(M, 64, M + K)
+    say(f"  rmsnorm full size M={M} K={K} had={had}")
+    codes, scales = tb.hbitlinear_quantize_rmsnorm(dev(x), dev(gain), 1e-6, 4, had)
+    torch.cuda.synchronize()
+    gq = codes_to_int8(codes, M, K, 4)[rows]
+    gs = scales.cpu().numpy()[rows]
+    del codes, scales
+    oq, os_ = oracle.quantize(oracle.rmsnorm(x[rows], gain, 1e-6), 4, had)
+    diff = gq.astype(np.int32) - oq.astype(np.int32)
+    assert np.count_nonzero(diff) <= 1e-4 * diff.size and np.all(np.abs(diff) <= 1)
+    assert np.allclose(gs, os_, rtol=1e-5, atol=0)
+
+
 # ------------------------------------------------- weight + activation Hadamard variant ----
 
 def test_weight_activation_hadamard_variant(tb):
