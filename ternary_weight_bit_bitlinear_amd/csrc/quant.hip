@@ -75,13 +75,13 @@ __host__ __device__ constexpr int num_groups(int L, int LE) { return 1 + (L - 2 
 
 // LDS index of element k: index bits 2.. XOR-ed with higher bits, so that 16-byte chunks stay
 // whole and the strided accesses of the exchanges spread over the banks (32 consecutive lanes
-// are served together).  For K >= 8192 bits 7..10 go into bits 2..5: with bits 8..10 only,
-// two lanes that differ in bit 7 of k meet in one bank (3-6 % slower there; smaller K measured
-// no different or faster with the narrower form).  Either form is its own inverse on [0, K).
+// are served together).  For K >= 4096 bits 7..10 go into bits 2..5: with bits 8..10 only,
+// two lanes that differ in bit 7 of k meet in one bank (1-6 % slower at K = 4096..16384;
+// K = 1024 measured faster with the narrower form).  Either form is its own inverse on [0, K).
 template <int L>
 __device__ __forceinline__ uint32_t swz(uint32_t k)
 {
-    if constexpr (L >= 13) return k ^ (((k >> 7) & 15u) << 2);
+    if constexpr (L >= 12) return k ^ (((k >> 7) & 15u) << 2);
     else return k ^ (((k >> 8) & 7u) << 2);
 }
 
