@@ -284,7 +284,11 @@ def cpu_baseline_decode(si, oracle, d, tb, min_seconds=10.0, max_seconds=30.0):
     M, K, N, L = d["M"], d["K"], d["N"], d["L"]
     xs = d["x"].cpu().numpy()
     unique = len(d["packs"])
-    packs = [(p.cpu().numpy(), g) for p, g in d["packs"]]
+    # the oracle's own packing of the same seeded matrices (make_decode's recipe)
+    packs = []
+    for u in range(unique):
+        p, g, _t = oracle.pack_weights(si.gaussian_weights(2, N, K, layer=u))
+        packs.append((p, g))
     layers = 0
     t0 = time.perf_counter()
     while layers < L:

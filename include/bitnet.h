@@ -68,9 +68,12 @@ int bitnet_abi_version(void);
  * Layout (this library's choice; the pages fix only the byte code):
  *   - which weights share a byte: row n is cut into blocks of 320 weights, 64 bytes each;
  *     byte b of block B holds the weights k = 320 B + b + 64 i as digit i (i = 0..4);
- *   - where a byte sits: rows go in groups of 16 (the last group padded with zero rows);
- *     group G and block B form one 1024-byte tile at offset (G * ceil(K/320) + B) * 1024, and
- *     byte b of row n sits in it at ((b / 16) * 16 + n % 16) * 16 + b % 16.
+ *   - canonical order of the bytes: row-major, byte b of block B of row n at
+ *     n * 64 * ceil(K/320) + 64 B + b (N * 64 * ceil(K/320) bytes);
+ *   - where a byte sits in this library's buffers (a permutation of the canonical order plus
+ *     pad rows): rows go in groups of 16 (the last group padded with zero rows); group G and
+ *     block B form one 1024-byte tile at offset (G * ceil(K/320) + B) * 1024, and byte b of
+ *     row n sits in it at ((b / 16) * 16 + n % 16) * 16 + b % 16.
  * Weights at k >= K and pad rows n >= N are t = 0.  Grouping weights 64 apart lets one
  * 16-byte load decode into five 64-wide MFMA slices, and the tile order lets one wave load
  * the 16 x 64 bytes of a tile as one contiguous kilobyte. */
@@ -115,8 +118,13 @@ int bitnet_pack_weights_segments(const float *W_host, int S, const int *seg_n, i
 int bitnet_pack_gate_up(const float *W_gate_host, const float *W_up_host, int F, int K,
                         uint8_t *packed_host, float *gate_scale_out, float *up_scale_out);
 
-/* Inverse of the packing: trits_host (N x K int8, host) receives t in {-1, 0, +1}.
- * Returns BITNET_ERR_FORMAT if a byte is > 242 or a padding position is not t = 0. */
+/* Inverse of the packing [2B4T write-up section 1.1: a byte holds five base-3 digits, the
+ * first most significant; digit d is the trit d - 1]: packed_host (bitnet_packed_bytes(N, K)
+ * bytes, host, in this library's tiled placement) is decoded into trits_host (N x K int8,
+ * host, row-major), t in {-1, 0, +1}; this defines the canonical order of the packed weights.
+ * Two passes: every byte is checked before anything is written, so on error trits_host is
+ * untouched.  Returns BITNET_ERR_FORMAT if a byte is > 242 or a padding position (k >= K or a
+ * pad row) is not t = 0. */
 int bitnet_unpack_weights(const uint8_t *packed_host, int N, int K, int8_t *trits_host);
 
 /* ------------------------------------------------------------------------------------ */
@@ -127,7 +135,11 @@ int bitnet_unpack_weights(const uint8_t *packed_host, int N, int K, int8_t *trit
  * the activation codes (hbitlinear_codes_bytes) and M fp32 scales, each 256-byte aligned. */
 int hbitlinear_workspace_bytes(int M, int K, int act_bits, size_t *bytes_out);
 
-/* H-BitLinear (use_hadamard = 1) or BitLinear (use_hadamard = 0) forward:
+/* H-BitLinear (use_hadamard = 1) or BitLinear (use_hadamard = 0) forward [v2 write-up,
+ * H-BitLinear passage: an online Hadamard transform of the activations before their
+ * quantisation, +1/-1 entries with orthogonal rows; BitNet v2 abstract (chatpaper.ai); 2B4T
+ * write-up section 1.2: absmax activations, absmean ternary weights, multiplications become
+ * add / subtract / skip; v2 write-up: no bias]:
  *   x_h = use_hadamard ? x H_K / sqrt(K) : x                (per token, Sylvester H_K)
  *   q, s = per-token absmax quantisation of x_h to act_bits  (Qp = 2^(b-1) - 1)
  *   out[m][n] = (float(sum_k q[m][k] t[n][k]) * s[m]) * w_scale

@@ -94,65 +94,53 @@ void bitnet_ref_ternarize(const float *W, int N, int K, int8_t *t, float *gamma_
 }
 
 /* ------------------------------------------------------------------------------------- */
-/* Packed weight layout.  The pages fix the byte code (five trits, base 3, MSB first) but    */
-/* not which five weights share a byte, nor where bytes sit.  Reading taken:                 */
-/*  - which weights share a byte: a row is cut into blocks of 320 weights (64 bytes); byte b */
-/*    of block B holds the weights k = 320 B + b + 64 i as digit i (i = 0..4);               */
-/*  - where the byte sits: rows are taken in groups of 16 (the last group padded with rows   */
-/*    of zero weights); group G and block B form one 1024-byte tile at offset                */
-/*    (G * nblk + B) * 1024, and inside it byte b of row n sits at                           */
-/*    ((b / 16) * 16 + n % 16) * 16 + b % 16.                                                */
-/* Weights past the end of a row (k >= K) and pad rows (n >= N) are t = 0 (digit 1).         */
+/* Packed weight matrix.  The pages fix the byte code (five trits, base 3, MSB first) but    */
+/* not which five weights share a byte.  Reading taken: a row is cut into blocks of 320      */
+/* weights (64 bytes); byte b of block B holds the weights k = 320 B + b + 64 i as digit i    */
+/* (i = 0..4).  Bytes are stored row-major: byte b of block B of row n is byte               */
+/* n * row_bytes + 64 B + b, row_bytes = 64 * ceil(K / 320).  Weights past the end of a row   */
+/* (k >= K) are t = 0 (digit 1).  Where a device keeps these bytes is its own affair: any     */
+/* other placement is a permutation of this array.                                          */
 /* ------------------------------------------------------------------------------------- */
 
 int64_t bitnet_ref_row_bytes(int K) { return 64 * (int64_t)((K + 319) / 320); }
 
-int64_t bitnet_ref_packed_bytes(int N, int K)
-{
-    return (int64_t)((N + 15) / 16) * 16 * bitnet_ref_row_bytes(K);
-}
-
-/* Byte offset of byte b of block B of row n. */
-int64_t bitnet_ref_packed_offset(int n, int B, int b, int K)
-{
-    int64_t nblk = (K + 319) / 320;
-    return ((int64_t)(n / 16) * nblk + B) * 1024 + (int64_t)((b / 16) * 16 + n % 16) * 16 + b % 16;
-}
+int64_t bitnet_ref_packed_bytes(int N, int K) { return (int64_t)N * bitnet_ref_row_bytes(K); }
 
 void bitnet_ref_pack(const int8_t *t, int N, int K, uint8_t *packed)
 {
     int nblk = (K + 319) / 320;
-    int rows = (N + 15) / 16 * 16;
-    for (int n = 0; n < rows; n++) {
+    int64_t rb = bitnet_ref_row_bytes(K);
+    for (int n = 0; n < N; n++) {
         for (int B = 0; B < nblk; B++) {
             for (int b = 0; b < 64; b++) {
                 int digits[5];
                 for (int i = 0; i < 5; i++) {
                     int64_t k = 320 * (int64_t)B + b + 64 * i;
-                    int tv = (n < N && k < K) ? t[(int64_t)n * K + k] : 0;
+                    int tv = k < K ? t[(int64_t)n * K + k] : 0;
                     digits[i] = tv + 1;
                 }
-                packed[bitnet_ref_packed_offset(n, B, b, K)] = (uint8_t)bitnet_ref_encode5(digits);
+                packed[(int64_t)n * rb + 64 * B + b] = (uint8_t)bitnet_ref_encode5(digits);
             }
         }
     }
 }
 
 /* Inverse of bitnet_ref_pack.  Returns 0, or -1 if a byte is not a base-3 code or a padding */
-/* position (k >= K or n >= N) holds a non-zero weight.                                     */
+/* position (k >= K) holds a non-zero weight.                                                */
 int bitnet_ref_unpack(const uint8_t *packed, int N, int K, int8_t *t)
 {
     int nblk = (K + 319) / 320;
-    int rows = (N + 15) / 16 * 16;
-    for (int n = 0; n < rows; n++) {
+    int64_t rb = bitnet_ref_row_bytes(K);
+    for (int n = 0; n < N; n++) {
         for (int B = 0; B < nblk; B++) {
             for (int b = 0; b < 64; b++) {
                 int digits[5];
-                if (bitnet_ref_decode5(packed[bitnet_ref_packed_offset(n, B, b, K)], digits) != 0)
+                if (bitnet_ref_decode5(packed[(int64_t)n * rb + 64 * B + b], digits) != 0)
                     return -1;
                 for (int i = 0; i < 5; i++) {
                     int64_t k = 320 * (int64_t)B + b + 64 * i;
-                    if (n < N && k < K) t[(int64_t)n * K + k] = (int8_t)(digits[i] - 1);
+                    if (k < K) t[(int64_t)n * K + k] = (int8_t)(digits[i] - 1);
                     else if (digits[i] != 1) return -1;
                 }
             }

@@ -99,6 +99,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _rows_k(x, name="x"):
+    if len(x.shape) != 2:
+        raise ValueError(f"{name} must be 2-D (M x K)")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def _packed_check(packed, rows: int, K: int, name: str) -> None:
+    # the kernels size their reads from N and K, not from the allocation: a short buffer would
+    # be read past its end on the device, so it is refused here, before anything else
+    if packed.numel() < bitnet_packed_bytes(rows, K):
+        raise ValueError(f"{name} holds {packed.numel()} bytes, the packed {rows} x {K} weight "
+                         f"needs {bitnet_packed_bytes(rows, K)}")
+
+
 def _dev_check(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -207,9 +221,10 @@ def hbitlinear_forward(x, N: int, act_bits: int, use_hadamard: bool, packed_w, w
                        out=None, workspace=None, stream=None):
     """out = H-BitLinear(x) for x (M x K fp32, device); returns out (M x N fp32, device)."""
     import torch
+    M, K = _rows_k(x)
+    _packed_check(packed_w, N, K, "packed_w")
     _dev_check(x, torch.float32, "x")
     _dev_check(packed_w, torch.uint8, "packed_w")
-    M, K = x.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _dev_check(out, torch.float32, "out")
@@ -239,11 +254,12 @@ def hbitlinear_forward_segments(x, seg_n, act_bits: int, use_hadamard: bool, pac
     bitnet_pack_weights_segments (device), seg_n / w_scales (host sequences of S) ->
     out (M x sum(seg_n) fp32, device)."""
     import torch
+    n, g = _seg_arrays(seg_n, w_scales)
+    M, K = _rows_k(x)
+    N = int(n.sum())
+    _packed_check(packed_w, N, K, "packed_w")
     _dev_check(x, torch.float32, "x")
     _dev_check(packed_w, torch.uint8, "packed_w")
-    n, g = _seg_arrays(seg_n, w_scales)
-    M, K = x.shape
-    N = int(n.sum())
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _dev_check(out, torch.float32, "out")
@@ -266,9 +282,10 @@ def hbitlinear_forward_swiglu(x, F: int, act_bits: int, use_hadamard: bool, pack
     """h = SiLU(gate(x)) * up(x): x (M x K fp32, device), packed_gate_up from
     bitnet_pack_gate_up (device) -> h (M x F fp32, device)."""
     import torch
+    M, K = _rows_k(x)
+    _packed_check(packed_gate_up, 2 * F, K, "packed_gate_up")
     _dev_check(x, torch.float32, "x")
     _dev_check(packed_gate_up, torch.uint8, "packed_gate_up")
-    M, K = x.shape
     if out is None:
         out = torch.empty((M, F), dtype=torch.float32, device=x.device)
     _dev_check(out, torch.float32, "out")
@@ -295,7 +312,9 @@ def hbitlinear_grouped_workspace_bytes(L: int, M: int, K: int, act_bits: int) ->
 def hbitlinear_forward_grouped(x, N: int, act_bits: int, use_hadamard: bool, packed_ptrs,
                                w_scales, out=None, workspace=None, stream=None):
     """L independent forwards: x (L x M x K fp32), packed_ptrs (int64 device tensor of L
-    device addresses of packed weights), w_scales (L fp32 device tensor) -> out (L x M x N)."""
+    device addresses of packed weights), w_scales (L fp32 device tensor) -> out (L x M x N).
+    The buffers behind packed_ptrs are not visible here: each must hold
+    bitnet_packed_bytes(N, K) bytes."""
     import torch
     _dev_check(x, torch.float32, "x")
     _dev_check(packed_ptrs, torch.int64, "packed_ptrs")
@@ -343,12 +362,11 @@ def bitnet_ternary_gemm_i32(codes, M: int, K: int, N: int, act_bits: int, packed
                             stream=None):
     """acc = sum_k q t (exact int32, M x N, device) from device codes and packed weights."""
     import torch
-    _dev_check(codes, torch.uint8, "codes")
-    _dev_check(packed_w, torch.uint8, "packed_w")
+    _packed_check(packed_w, N, K, "packed_w")
     if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits):
         raise ValueError("codes buffer is too small")
-    if packed_w.numel() < bitnet_packed_bytes(N, K):
-        raise ValueError("packed_w buffer is too small")
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(packed_w, torch.uint8, "packed_w")
     if acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
     _dev_check(acc, torch.int32, "acc")
@@ -473,10 +491,11 @@ def hbitlinear_forward_rmsnorm(x, gain, eps: float, N: int, act_bits: int, use_h
                                packed_w, w_scale: float, out=None, workspace=None, stream=None):
     """out = forward(RMSNorm(x) * gain) for x (M x K fp32, device)."""
     import torch
+    M, K = _rows_k(x)
+    _packed_check(packed_w, N, K, "packed_w")
     _dev_check(x, torch.float32, "x")
     _dev_check(gain, torch.float32, "gain")
     _dev_check(packed_w, torch.uint8, "packed_w")
-    M, K = x.shape
     if gain.numel() < K:
         raise ValueError("gain needs K entries")
     if out is None:

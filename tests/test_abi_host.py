@@ -12,6 +12,7 @@ import oracle
 import seeded_inputs as si
 import ternary_weight_bit_bitlinear_amd as tb
 from conftest import ROOT
+from packed_layout import device_groups, from_device, to_device
 
 HEADER = os.path.join(ROOT, "include", "bitnet.h")
 
@@ -50,6 +51,10 @@ def test_abi_version_and_status_strings():
     assert tb.bitnet_status_string(-99) == "unknown status"
 
 
+# The product packer against the oracle's canonical row-major bytes, three ways: the trits the
+# product's unpacker reads back are the oracle's; the product's bytes are the canonical bytes
+# placed by the documented tile permutation (pad rows all 121); and, read back through the
+# inverse permutation, they decode with the oracle's unpacker to the same trits.
 @pytest.mark.parametrize("N,K", [(1, 1), (3, 5), (4, 64), (7, 319), (5, 320), (9, 321),
                                  (16, 1000), (256, 256), (64, 4096), (33, 16384)])
 def test_packer_matches_oracle_bytes(N, K):
@@ -57,16 +62,37 @@ def test_packer_matches_oracle_bytes(N, K):
     packed, g = tb.bitnet_pack_weights(W)
     opacked, og, ot = oracle.pack_weights(W)
     assert np.float32(g) == og
-    assert packed.size == oracle.packed_bytes(N, K) == tb.bitnet_packed_bytes(N, K)
-    assert np.array_equal(packed, opacked)
+    assert opacked.size == oracle.packed_bytes(N, K) == N * 64 * ((K + 319) // 320)
+    assert packed.size == tb.bitnet_packed_bytes(N, K) == (N + 15) // 16 * 16 * 64 * ((K + 319) // 320)
     assert np.array_equal(tb.bitnet_unpack_weights(packed, N, K), ot)
+    assert np.array_equal(packed, to_device(opacked, N, K))
+    assert np.array_equal(oracle.unpack(from_device(packed, N, K), N, K), ot)
 
 
 def test_packer_matches_oracle_at_full_size():
     W = si.gaussian_weights(3, 4096, 4096)
     packed, g = tb.bitnet_pack_weights(W)
-    opacked, og, _ = oracle.pack_weights(W)
-    assert np.float32(g) == og and np.array_equal(packed, opacked)
+    opacked, og, ot = oracle.pack_weights(W)
+    assert np.float32(g) == og and np.array_equal(packed, to_device(opacked, 4096, 4096))
+    assert np.array_equal(tb.bitnet_unpack_weights(packed, 4096, 4096), ot)
+
+
+def test_device_permutation_helper_is_a_bijection():
+    # the helper's permutation: every canonical byte lands on its own device byte, pad rows
+    # hold 121, and from_device inverts it
+    N, K = 35, 700
+    nb = (K + 319) // 320
+    canon = np.arange(N * 64 * nb, dtype=np.int64)
+    dev = to_device((canon % 241).astype(np.uint8), N, K)
+    assert dev.size == 48 * 64 * nb
+    assert np.array_equal(from_device(dev, N, K), (canon % 241).astype(np.uint8))
+    # positions: row 1 of a tile follows row 0 by 16 bytes; the tile of block 1 starts at 1 KB
+    idx = to_device(np.zeros(N * 64 * nb, np.uint8), N, K)
+    assert np.count_nonzero(idx == 121) == (48 - N) * 64 * nb
+    one = np.zeros((N, 64 * nb), np.uint8); one[1, 0] = 7; one[0, 64] = 9; one[20, 64 + 10] = 5
+    d = to_device(one.reshape(-1), N, K)
+    assert d[16] == 7 and d[1024] == 9
+    assert d[(1 * nb + 1) * 1024 + (0 * 16 + 4) * 16 + 10] == 5
 
 
 def test_packer_zero_and_worked_example():
@@ -160,11 +186,6 @@ def test_stage_validation():
 
 # --------------------------------------------- stacked and gate / up weight layouts ----
 
-def _groups(packed, K):
-    g = 1024 * ((K + 319) // 320)
-    return packed.reshape(-1, g)
-
-
 @pytest.mark.parametrize("seg_n,K", [([16, 32, 48], 640), ([4096 // 8, 1024 // 8, 1024 // 8], 1024),
                                      ([16], 320)])
 def test_pack_segments_is_the_concatenation_of_separate_packs(seg_n, K):
@@ -172,7 +193,7 @@ def test_pack_segments_is_the_concatenation_of_separate_packs(seg_n, K):
     packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
     parts = [oracle.pack_weights(W) for W in Ws]
     assert packed.size == tb.bitnet_packed_bytes(sum(seg_n), K)
-    assert np.array_equal(packed, np.concatenate([p for p, _, _ in parts]))
+    assert np.array_equal(packed, np.concatenate([to_device(p, n, K) for (p, _, _), n in zip(parts, seg_n)]))
     assert np.array_equal(gs, np.array([g for _, g, _ in parts], np.float32))
     # and the stacked buffer decodes to the stacked trits
     assert np.array_equal(tb.bitnet_unpack_weights(packed, sum(seg_n), K),
@@ -187,10 +208,10 @@ def test_pack_gate_up_interleaves_16_row_groups(F, K):
     pg, og, tg = oracle.pack_weights(Wg)
     pu, ou, tu = oracle.pack_weights(Wu)
     assert (np.float32(gg), np.float32(gu)) == (og, ou)
-    G = _groups(packed, K)
+    G = device_groups(packed, K)
     assert G.shape[0] == 2 * F // 16
-    assert np.array_equal(G[0::2], _groups(pg, K))
-    assert np.array_equal(G[1::2], _groups(pu, K))
+    assert np.array_equal(G[0::2], device_groups(to_device(pg, F, K), K))
+    assert np.array_equal(G[1::2], device_groups(to_device(pu, F, K), K))
     t = tb.bitnet_unpack_weights(packed, 2 * F, K).reshape(F // 16, 2, 16, K)
     assert np.array_equal(t[:, 0].reshape(F, K), tg)
     assert np.array_equal(t[:, 1].reshape(F, K), tu)
@@ -266,7 +287,7 @@ def test_pack_weights_hadamard_matches_oracle_bytes(N, K):
     packed, g = tb.bitnet_pack_weights_hadamard(W)
     opacked, og = oracle.pack_weights_hadamard(W)
     assert np.float32(g) == og
-    assert np.array_equal(packed, opacked)
+    assert np.array_equal(packed, to_device(opacked, N, K))
 
 
 def test_pack_weights_hadamard_validation():
@@ -275,3 +296,28 @@ def test_pack_weights_hadamard_validation():
     assert L.bitnet_pack_weights_hadamard(FAKE, 4, 320, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
     assert L.bitnet_pack_weights_hadamard(FAKE, 4, 128, FAKE, FAKE) == tb.BITNET_ERR_UNSUPPORTED
     assert L.bitnet_pack_weights_hadamard(FAKE, 0, 256, FAKE, FAKE) == tb.BITNET_ERR_SHAPE
+
+
+# The binding refuses a packed weight buffer shorter than bitnet_packed_bytes for the rows the
+# call reads (N, sum(seg_n), 2 F) before it looks at devices or calls the library: the kernels
+# size their reads from the shape, so a short buffer would be read past its end on the GPU.
+def test_binding_refuses_short_packed_weights():
+    torch = pytest.importorskip("torch")
+    M, K, N, F = 4, 640, 48, 32
+    x = torch.zeros((M, K), dtype=torch.float32)
+    g = torch.ones(K, dtype=torch.float32)
+    seg = [16, 16, 32]
+    cases = [
+        (lambda p: tb.hbitlinear_forward(x, N, 8, False, p, 1.0), N),
+        (lambda p: tb.hbitlinear_forward_rmsnorm(x, g, 1e-6, N, 8, False, p, 1.0), N),
+        (lambda p: tb.hbitlinear_forward_segments(x, seg, 8, False, p, [1.0, 1.0, 1.0]), sum(seg)),
+        (lambda p: tb.hbitlinear_forward_swiglu(x, F, 8, False, p, 1.0, 1.0), 2 * F),
+        (lambda p: tb.bitnet_ternary_gemm_i32(torch.zeros(M * K, dtype=torch.uint8), M, K, N, 8, p), N),
+    ]
+    for call, rows in cases:
+        need = tb.bitnet_packed_bytes(rows, K)
+        with pytest.raises(ValueError, match="packed"):
+            call(torch.zeros(need - 1, dtype=torch.uint8))
+        # a buffer of the right size passes this check and stops at the device check instead
+        with pytest.raises(TypeError):
+            call(torch.zeros(need, dtype=torch.uint8))

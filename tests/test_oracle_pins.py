@@ -63,7 +63,7 @@ def test_pack_groups_five_weights_per_byte():
     t = np.zeros((2, K), np.int8)
     t[0, [0, 64, 128, 192, 256]] = [1, -1, 0, 1, 0]
     p = oracle.pack(t)
-    assert p.shape == (1024,)                   # rows padded to a group of 16: one tile
+    assert p.shape == (128,)                    # two rows of one 64-byte block, row-major
     assert p[0] == 178
     assert np.all(p[1:] == 121)                 # all-zero trits: digits 1,1,1,1,1 = 121
     assert oracle.encode5([1, 1, 1, 1, 1]) == 121
@@ -75,27 +75,38 @@ def test_pack_roundtrip_and_size(N, K):
     rng = np.random.default_rng(N * 1000 + K)
     t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
     p = oracle.pack(t)
-    assert p.size == ((N + 15) // 16) * 16 * 64 * ((K + 319) // 320)
+    assert p.size == N * 64 * ((K + 319) // 320)
     assert p.max() <= 242
     assert np.array_equal(oracle.unpack(p, N, K), t)
 
 
-def test_pack_tile_placement_is_a_bijection():
-    # every (row, block, byte) of the padded matrix has its own offset, tiles are contiguous
-    N, K = 35, 700
-    nblk = (K + 319) // 320
-    rows = (N + 15) // 16 * 16
-    offs = [oracle.packed_offset(n, B, b, K) for n in range(rows) for B in range(nblk) for b in range(64)]
-    assert sorted(offs) == list(range(oracle.packed_bytes(N, K)))
-    # the 16 rows of a tile at the same 16-byte chunk are consecutive 16-byte runs
-    assert oracle.packed_offset(1, 0, 0, K) - oracle.packed_offset(0, 0, 0, K) == 16
-    assert oracle.packed_offset(0, 0, 16, K) - oracle.packed_offset(15, 0, 15, K) == 1
-    assert oracle.packed_offset(0, 1, 0, K) == 1024
-    # the decoded trits of a single byte land where the layout says
-    t = np.zeros((N, K), np.int8)
-    t[20, [330, 394, 458, 522, 586]] = [1, -1, 0, 1, 0]       # block 1, byte 10, row 20
+def test_pack_byte_positions_brute_force():
+    # every byte decoded by hand (base-3 digits by repeated division) against the trits it
+    # should hold: byte b of block B of row n is byte n * row_bytes + 64 B + b and holds
+    # k = 320 B + b + 64 i as digit i, most significant first; pad weights are t = 0
+    N, K = 3, 700
+    rng = np.random.default_rng(5)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
     p = oracle.pack(t)
-    assert p[oracle.packed_offset(20, 1, 10, K)] == 178
+    rb = 64 * 3
+    for n in range(N):
+        for B in range(3):
+            for b in range(64):
+                v = int(p[n * rb + 64 * B + b])
+                digs = []
+                for _ in range(5):
+                    digs.append(v % 3)
+                    v //= 3
+                digs = digs[::-1]
+                for i in range(5):
+                    k = 320 * B + b + 64 * i
+                    assert digs[i] - 1 == (t[n, k] if k < K else 0)
+    # the page's byte at a block other than the first
+    t = np.zeros((N, K), np.int8)
+    t[2, [330, 394, 458, 522, 586]] = [1, -1, 0, 1, 0]       # block 1, byte 10, row 2
+    p = oracle.pack(t)
+    assert p[2 * rb + 64 + 10] == 178
+    assert np.count_nonzero(p != 121) == 1
 
 
 def test_unpack_rejects_bad_bytes():
