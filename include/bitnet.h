@@ -19,7 +19,8 @@
  *   - Shapes: x is M x K fp32 row-major (one token per row); the weight is N x K
  *     (nn.Linear convention, y = x W^T); out is M x N fp32 row-major.
  *   - The caller owns every buffer.  The library never allocates or frees device memory and
- *     keeps no state between calls, so calls are thread-safe.
+ *     keeps no state between calls, so calls are thread-safe -- except
+ *     hbitlinear_forward_noalloc, whose workspace is one static array per device (see there).
  *   - "Device" pointers are HIP device memory on the current device; "host" pointers are
  *     ordinary CPU memory.  `stream` is a hipStream_t passed as void* (NULL = null stream).
  *   - Argument checks run on the host before anything is launched; a failing check launches
@@ -149,6 +150,24 @@ int hbitlinear_workspace_bytes(int M, int K, int act_bits, size_t *bytes_out);
 int hbitlinear_forward(const float *x, int M, int K, int N, int act_bits, int use_hadamard,
                        float *out, const uint8_t *packed_w, float w_scale, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): hbitlinear_forward with its workspace taken from
+ * a static device array of BITNET_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends, instead of a caller buffer.  Same arguments (minus
+ * the workspace), same arithmetic, same result bit for bit.  It calls no allocating routine;
+ * the first call on a device looks up that device's copy of the array (call it once outside
+ * graph capture if the first real call is captured).  Every call on one GPU shares that GPU's
+ * array, and nothing in it needs to start at any value (the activation stage writes the codes
+ * and scales before the product reads them), so calls that overlap in time on one GPU -- on
+ * different streams, or from different threads -- race and must be serialised by the caller.
+ * Returns BITNET_ERR_WORKSPACE when hbitlinear_workspace_bytes(M, K, act_bits) exceeds
+ * BITNET_NOALLOC_SCRATCH_BYTES (for example INT4 with M * K / 2 + 4 M above 16 MiB), before
+ * touching the GPU; other rules as hbitlinear_forward. */
+#define BITNET_NOALLOC_SCRATCH_BYTES (16u << 20)
+int hbitlinear_forward_noalloc(const float *x, int M, int K, int N, int act_bits,
+                               int use_hadamard, float *out, const uint8_t *packed_w,
+                               float w_scale, void *stream);
 
 /* L independent forwards of one shape in a single call -- e.g. a stack of layers whose
  * inputs are already held separately, or projections of one block -- each exactly as

@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_workspace_bytes": ([I, I, I, PSZ], I),
             "hbitlinear_codes_bytes": ([I, I, I, PSZ], I),
             "hbitlinear_forward": ([P, I, I, I, I, I, P, P, F, P, SZ, P], I),
+            "hbitlinear_forward_noalloc": ([P, I, I, I, I, I, P, P, F, P], I),
             "hbitlinear_quantize": ([P, I, I, I, I, P, P, P, P], I),
             "bitnet_ternary_gemm_i32": ([P, I, I, I, I, P, P, P], I),
             "hbitlinear_gemm_dequant": ([P, P, I, I, I, I, P, F, P, P], I),
@@ -237,6 +238,28 @@ def hbitlinear_forward(x, N: int, act_bits: int, use_hadamard: bool, packed_w, w
     _check(lib().hbitlinear_forward(_ptr(x), M, K, N, act_bits, int(bool(use_hadamard)),
                                     _ptr(out), _ptr(packed_w), float(w_scale), _ptr(workspace),
                                     workspace.numel(), _stream(stream)), "hbitlinear_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # BITNET_NOALLOC_SCRATCH_BYTES
+
+
+def hbitlinear_forward_noalloc(x, N: int, act_bits: int, use_hadamard: bool, packed_w,
+                               w_scale: float, out, stream=None):
+    """hbitlinear_forward with the library's static device workspace: x (M x K fp32, device),
+    out (M x N fp32, device, the caller's: nothing is allocated here or in the library).
+    Calls that overlap on one GPU race on the shared workspace."""
+    import torch
+    M, K = _rows_k(x)
+    _packed_check(packed_w, N, K, "packed_w")
+    if out.numel() < M * N:
+        raise ValueError("out is too small")
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    _dev_check(out, torch.float32, "out")
+    _check(lib().hbitlinear_forward_noalloc(_ptr(x), M, K, N, act_bits, int(bool(use_hadamard)),
+                                            _ptr(out), _ptr(packed_w), float(w_scale),
+                                            _stream(stream)), "hbitlinear_forward_noalloc")
     return out
 
 

@@ -1,11 +1,45 @@
 // abi.hip -- the extern "C" entry points of libbitnet_hip.so (declared in include/bitnet.h).
 // Every entry point checks its arguments on the host first and launches nothing when a check
 // fails; work is queued on the caller's stream.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 using namespace bitnet;
 
 namespace {
+
+// Workspace of hbitlinear_forward_noalloc: the activation codes and scales of one call live in
+// this array, which the HIP runtime places in each device's memory when the library's code is
+// loaded there and keeps until the process ends.  Host code never uses the name itself as an
+// address (on the host it is only a handle): the device address is looked up once per device
+// with hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[BITNET_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// The current device's copy of `scratch`, resolved on the first call on that device.
+int scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return BITNET_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return BITNET_ERR_UNSUPPORTED;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return BITNET_ERR_HIP;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BITNET_OK;
+}
 
 int check_shape(int M, int K, int N, int bits, int use_hadamard)
 {
@@ -195,6 +229,28 @@ int hbitlinear_forward(const float* x, int M, int K, int N, int act_bits, int us
     if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
         return BITNET_ERR_WORKSPACE;
     uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 w_scale, out, nullptr, s));
+}
+
+int hbitlinear_forward_noalloc(const float* x, int M, int K, int N, int act_bits, int use_hadamard,
+                               float* out, const uint8_t* packed_w, float w_scale, void* stream)
+{
+    if (x == nullptr || out == nullptr || packed_w == nullptr) return BITNET_ERR_NULL;
+    int rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    // the same workspace layout as hbitlinear_forward, inside the static array
+    if (workspace_bytes(M, K, act_bits) > (size_t)BITNET_NOALLOC_SCRATCH_BYTES)
+        return BITNET_ERR_WORKSPACE;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != BITNET_OK) return rc;
+    uint8_t* codes = static_cast<uint8_t*>(ws);
     float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);

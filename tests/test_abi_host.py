@@ -321,3 +321,20 @@ def test_binding_refuses_short_packed_weights():
         # a buffer of the right size passes this check and stops at the device check instead
         with pytest.raises(TypeError):
             call(torch.zeros(need, dtype=torch.uint8))
+
+
+def test_noalloc_validation_without_launch():
+    # checks that fail return before the entry point touches the GPU (no device here)
+    L = tb.lib()
+    f = ctypes.c_float(1.0)
+    assert L.hbitlinear_forward_noalloc(NUL, 4, 256, 64, 8, 1, FAKE, FAKE, f, NUL) == tb.BITNET_ERR_NULL
+    assert L.hbitlinear_forward_noalloc(FAKE, 4, 200, 64, 8, 1, FAKE, FAKE, f, NUL) == \
+        tb.BITNET_ERR_UNSUPPORTED
+    assert L.hbitlinear_forward_noalloc(FAKE, 0, 256, 64, 8, 1, FAKE, FAKE, f, NUL) == tb.BITNET_ERR_SHAPE
+    # the workspace limit: 16 MiB of codes and scales
+    assert tb.hbitlinear_workspace_bytes(8192, 4096, 4) > tb.NOALLOC_SCRATCH_BYTES
+    assert L.hbitlinear_forward_noalloc(FAKE, 8192, 4096, 64, 4, 1, FAKE, FAKE, f, NUL) == \
+        tb.BITNET_ERR_WORKSPACE
+    assert L.hbitlinear_forward_noalloc(FAKE, 4096, 4096, 64, 8, 0, FAKE, FAKE, f, NUL) == \
+        tb.BITNET_ERR_WORKSPACE
+    assert tb.hbitlinear_workspace_bytes(4096, 4096, 4) <= tb.NOALLOC_SCRATCH_BYTES
