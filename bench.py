@@ -1,17 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the H-BitLinear forward on one MI355X.
 
-Headline workload: plain BitLinear W1.58A8 at decode shape (M = 16 tokens, K = N = 4096, INT8
-activations, no Hadamard) over L = 128 distinct weight matrices (430 MB, more than the 256 MB
-Infinity Cache, so the weights stream from HBM).  One step = the activation stage over the
-L*M token rows and one grouped product launch over the L layers -- exactly the two kernels
-hbitlinear_forward_grouped runs.  tokens/s counts a token once per layer forward:
-value = M * L * steps / time.  The same layers run one call after another are reported too
-("decode_sequential").
+Headline workload: all seven linears of one 7B-class BitNet v2 block in batched prefill,
+M = 16384 tokens, hidden 4096, FFN 8192, INT4 activations: Q, K, V, gate and up are BitLinear
+on N(0,1) inputs, Wo (K = 4096) and Wdown (K = 8192) H-BitLinear on outlier-heavy inputs.  One
+step = the four activation stages (Q/K/V share one, gate/up another) and the seven product
+launches.  value = M * steps / time (tokens/s through the whole block); the roofline object is
+the product kernel's int8 matrix-core rate against the 5.0 POPS dense int8 peak.
 
-Also reported (same JSON line): decode at M = 1 and 4, and the large-M H-BitLinear workloads
-(Wo M=4096 K=N=4096; Wdown M=8192 K=16384 N=4096; all seven linears of a 7B block at
-M=16384), each with its int8 MFMA roofline fraction.
+Also reported (same JSON line): decode shapes (plain BitLinear W1.58A8, K = N = 4096, grouped
+over 128 distinct weight matrices and layer by layer, M = 16, 4, 1) against HBM bandwidth on the
+packed weights; Wo (M = 4096) and Wdown (M = 8192) alone; the block with fused launches; the
+activation stage with the RMS norm; the tiny parity configuration (M = 16, K = N = 256).
 
 Inputs are seeded synthetic data (seeded_inputs) resident in HBM before timing starts.
 """
@@ -42,10 +42,11 @@ def parse_args():
     p.add_argument("--large-steps", type=int, default=10)
     p.add_argument("--no-large", action="store_true", help="skip the large-M workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["headline", "decode", "wo", "wdown", "block", "block_fused"],
+    p.add_argument("--only", choices=["headline", "decode", "decode_grouped", "wo", "wdown",
+                                      "block_fused", "tiny"],
                    default=None,
-                   help="run one workload only (profiling); 'headline' is the grouped decode "
-                        "launch alone, without the sequential and other-M decode runs")
+                   help="run one workload only (profiling): 'headline' is the 7B block alone; "
+                        "'decode_grouped' the grouped M = --M decode launch alone")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device-to-device copy of --copy-mib MiB five times "
                         "(the reference point for the HBM byte counters)")
@@ -336,6 +337,7 @@ def cpu_baseline_large(si, oracle, config, rows_max=256, chunk=16):
 KERNEL_SOURCES = {
     "gemm_decode_kernel": ["gemm_decode.hip", "common.h"],
     "gemm_tern_kernel": ["gemm.hip", "common.h"],
+    "gemm_tern4_kernel": ["gemm.hip", "common.h"],
     "quantize_rows_kernel": ["quant.hip", "common.h"],
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -612,6 +614,7 @@ def run_large(torch, tb, si, config, steps, warmup):
         else:
             per[lin.name].update(quant_shared=True)
     res = dict(workload=wl.name, M=M, ms_per_step=1e3 * dt / steps,
+               ops_per_step=ops, gemm_us_per_step=1e6 * gemm_s,
                tokens_per_s=M * steps / dt, int_tops=ops * steps / dt / 1e12,
                gemm_int_tops=ops / gemm_s / 1e12,
                gemm_mfma_frac=ops / gemm_s / 1e12 / INT8_PEAK_TOPS,
@@ -761,6 +764,113 @@ def run_k1_rmsnorm(torch, tb, si, steps):
     return out
 
 
+def run_tiny(torch, tb, si, steps=50):
+    """The tiny parity configuration (M = 16, K = N = 256, H-BitLinear INT8): one forward per
+    step, HIP events around each call; launch latency dominates at this size."""
+    lin = si.workload(1).linears[0]
+    x = torch.from_numpy(si.activations(1, lin)).cuda()
+    packed, g = tb.bitnet_pack_weights(si.weights(1, lin))
+    pw = torch.from_numpy(packed).cuda()
+    out = torch.empty((lin.M, lin.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tb.hbitlinear_workspace_bytes(lin.M, lin.K, lin.act_bits), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        tb.hbitlinear_forward(x, lin.N, lin.act_bits, lin.use_hadamard, pw, g, out=out, workspace=ws)
+    t = Timer(torch, steps)
+    for _ in range(steps):
+        t.begin(stream)
+        tb.hbitlinear_forward(x, lin.N, lin.act_bits, lin.use_hadamard, pw, g, out=out, workspace=ws,
+                              stream=stream)
+        t.end(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * t.mean_ms()
+    return dict(workload=f"hbitlinear_int8_tiny_M{lin.M}_K{lin.K}_N{lin.N}", forward_us=us,
+                tokens_per_s=lin.M / (us * 1e-6))
+
+
+def cpu_baseline_tiny(si, oracle, min_seconds=3.0):
+    """The oracle forward of the tiny configuration, repeated for at least `min_seconds`."""
+    lin = si.workload(1).linears[0]
+    x = si.activations(1, lin)
+    packed, g, _t = oracle.pack_weights(si.weights(1, lin))
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        oracle.forward(x, packed, g, lin.N, lin.act_bits, lin.use_hadamard)
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=lin.M * n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} forwards of the whole M={lin.M} K={lin.K} N={lin.N} configuration, "
+                       f"{dt:.1f} s")
+
+
+def decode_report(torch, tb, si, args):
+    """Decode shapes: grouped over L distinct matrices (M = --M, then 1 and 4) and layer by
+    layer.  The HBM fraction counts the packed weights at five trits per byte only; the codes,
+    scales and outputs a launch also moves are reported beside it."""
+    out = {}
+    log(f"[bench] decode: preparing M={args.M}, {args.layers} layers")
+    d = make_decode(torch, tb, si, args.M, args.layers)
+    M, K, N, L = d["M"], d["K"], d["N"], d["L"]
+    weight_bytes = L * canonical_packed_bytes(N, K)
+    r = run_decode_grouped(torch, tb, d, args.steps, args.warmup)
+    gbs = weight_bytes / (r["gemm_us"] * 1e-6) / 1e9
+    traffic = recorded_traffic("gemm_decode_kernel", f"M{M}_L{L}")
+    out["grouped"] = dict(
+        workload=f"bitlinear_w158a8_decode_M{M}_K{K}_N{N}_grouped_L{L}",
+        launch="one grouped product launch over L distinct weight matrices (the layers' weights "
+               "together exceed the Infinity Cache), after one activation stage over L*M rows",
+        tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"], int_tops=r["int_tops"],
+        quant_kernel_us=r["quant_us"],
+        roofline={"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                  "kernel": "gemm_decode_kernel<8,true,4,0>", "launch_us": r["gemm_us"],
+                  "launch_us_median": r["gemm_us_median"],
+                  "algorithmic_bytes_per_launch": weight_bytes,
+                  "other_bytes_per_launch": L * (M * K + 4 * M + 4 * M * N)})
+    log(f"[bench] decode grouped M={M}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.1f} us "
+        f"({gbs:.0f} GB/s on packed weights), quant {r['quant_us']:.1f} us")
+    if args.only == "decode_grouped":
+        return out
+    rs = run_decode(torch, tb, d, max(2, args.steps // 4), 1)
+    wl_bytes = canonical_packed_bytes(N, K)
+    out["sequential"] = dict(
+        launch="per layer: one activation stage and one product launch",
+        tokens_per_s=rs["tokens_per_s"], us_per_layer=rs["us_per_layer"],
+        timed_as="the steps captured as a HIP graph, one replay timed; launch times from HIP "
+                 "events in an eager pass",
+        gemm_us_per_layer=rs["gemm_us"], quant_us_per_layer=rs["quant_us"],
+        weight_gbs=wl_bytes / (rs["gemm_us"] * 1e-6) / 1e9,
+        hbm_frac=wl_bytes / (rs["gemm_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        hbm_frac_per_layer_step=wl_bytes / (rs["us_per_layer"] * 1e-6) / 1e9 / HBM_PEAK_GBS)
+    log(f"[bench] decode sequential: {rs['tokens_per_s']:.4g} tokens/s ({rs['us_per_layer']:.2f} us "
+        f"per layer), gemm launch {rs['gemm_us']:.2f} us")
+    for m in (1, 4):
+        dm = make_decode(torch, tb, si, m, args.layers)
+        rm = run_decode_grouped(torch, tb, dm, max(2, args.steps // 2), 1)
+        g2 = weight_bytes / (rm["gemm_us"] * 1e-6) / 1e9
+        out[f"grouped_M{m}"] = dict(tokens_per_s=rm["tokens_per_s"], gemm_us=rm["gemm_us"],
+                                    weight_gbs=g2, hbm_frac=g2 / HBM_PEAK_GBS,
+                                    quant_kernel_us=rm["quant_us"])
+        log(f"[bench] decode grouped M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm "
+            f"{rm['gemm_us']:.1f} us ({g2:.0f} GB/s on packed weights)")
+        del dm
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_baseline_decode(si, oracle, d, tb, min_seconds=5.0, max_seconds=15.0)
+        nthr = oracle.num_threads()
+        oracle.set_num_threads(1)
+        try:
+            out["cpu_baseline_1thread"] = cpu_baseline_decode(si, oracle, d, tb, min_seconds=2.0,
+                                                              max_seconds=6.0)
+        finally:
+            oracle.set_num_threads(nthr)
+    del d
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -791,47 +901,21 @@ def main():
         return
 
     result = {}
-    if args.only in (None, "decode", "headline"):
-        log(f"[bench] decode: preparing M={args.M}, {args.layers} layers")
-        d = make_decode(torch, tb, si, args.M, args.layers)
-        log("[bench] decode: timing (grouped)")
-        r = run_decode_grouped(torch, tb, d, args.steps, args.warmup)
-        log(f"[bench] decode grouped: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_us']:.1f} us "
-            f"({r['gemm_gbs']:.0f} GB/s), quant {r['quant_us']:.1f} us")
-        sequential, others = None, {}
-        if args.only != "headline":
-            rs = run_decode(torch, tb, d, max(2, args.steps // 4), 1)
-            log(f"[bench] decode sequential: {rs['tokens_per_s']:.4g} tokens/s "
-                f"({rs['us_per_layer']:.2f} us per layer, graph-timed), gemm launch "
-                f"{rs['gemm_us']:.2f} us ({rs['gemm_gbs']:.0f} GB/s)")
-            sequential = dict(tokens_per_s=rs["tokens_per_s"], us_per_layer=rs["us_per_layer"],
-                              timed_as="the steps captured as a HIP graph, one replay timed; "
-                                       "launch times from HIP events in an eager pass",
-                              gemm_us_per_layer=rs["gemm_us"],
-                              quant_us_per_layer=rs["quant_us"], gemm_gbs=rs["gemm_gbs"],
-                              hbm_frac=rs["gemm_gbs"] / HBM_PEAK_GBS)
-        for m in ((1, 4) if args.only != "headline" else ()):
-            dm = make_decode(torch, tb, si, m, args.layers)
-            rm = run_decode_grouped(torch, tb, dm, max(2, args.steps // 2), 1)
-            others[f"M{m}"] = dict(tokens_per_s=rm["tokens_per_s"], gemm_us=rm["gemm_us"],
-                                   gemm_gbs=rm["gemm_gbs"], hbm_frac=rm["gemm_gbs"] / HBM_PEAK_GBS)
-            log(f"[bench] decode grouped M={m}: {rm['tokens_per_s']:.4g} tokens/s, gemm "
-                f"{rm['gemm_us']:.1f} us ({rm['gemm_gbs']:.0f} GB/s)")
-            del dm
-        cpu = cpu1 = None
-        if not args.no_cpu_baseline and args.only != "headline":
+    if args.only in (None, "headline"):
+        # the headline: all seven linears of the 7B block (configuration 5)
+        log("[bench] block (headline): preparing")
+        r = run_large(torch, tb, si, 5, args.steps, args.warmup)
+        launches = len(r["linears"])
+        k2_us = r["gemm_us_per_step"] / launches
+        ops_launch = r["ops_per_step"] / launches
+        tops = ops_launch / (k2_us * 1e-6) / 1e12
+        log(f"[bench] block: {r['tokens_per_s']:.4g} tokens/s, product kernel {tops:.0f} TOP/s "
+            f"({100 * tops / INT8_PEAK_TOPS:.1f}% of int8 peak), mean launch {k2_us:.1f} us")
+        cpu = None
+        if not args.no_cpu_baseline:
             import oracle
-            log("[bench] cpu baseline (oracle)")
-            cpu = cpu_baseline_decode(si, oracle, d, tb)
-            # the same oracle on one host thread, as context
-            nthr = oracle.num_threads()
-            oracle.set_num_threads(1)
-            try:
-                cpu1 = cpu_baseline_decode(si, oracle, d, tb, min_seconds=3.0, max_seconds=10.0)
-            finally:
-                oracle.set_num_threads(nthr)
-        workload = f"bitlinear_w158a8_decode_M{d['M']}_K4096_N4096_grouped_L{d['L']}"
-        traffic = recorded_traffic("gemm_decode_kernel", f"M{d['M']}_L{d['L']}")
+            cpu = cpu_baseline_large(si, oracle, 5)
+            log(f"[bench] block: cpu oracle {cpu['value']:.4g} tokens/s ({cpu['sample']})")
         result = {
             "metric": METRIC,
             "value": r["tokens_per_s"],
@@ -845,32 +929,46 @@ def main():
             "vs_baseline": None,
             "dtype": "int8",
             "data": "synthetic",
-            "config": {"workload": workload,
-                       "M": d["M"], "K": 4096, "N": 4096, "layers": d["L"], "act_bits": 8,
-                       "use_hadamard": False,
-                       "step": "activation stage over L*M rows + one grouped product launch over "
-                               "L distinct weight matrices (hbitlinear_forward_grouped)",
-                       "timed_as": "the K steps captured once as a HIP graph and replayed; "
-                                   "launch_us from HIP events around each launch in an eager pass",
-                       "tokens_per_s": "M * layers * steps / seconds (a token counts once per layer)"},
+            "config": {"workload": r["workload"], "M": r["M"], "hidden": 4096, "ffn": 8192,
+                       "act_bits": 4,
+                       "linears": "q, k, v (4096->4096), gate, up (4096->8192): BitLinear on "
+                                  "N(0,1) inputs; wo (4096->4096), wdown (8192->4096): H-BitLinear "
+                                  "on outlier-heavy inputs",
+                       "step": "4 activation-stage launches (q/k/v and gate/up share theirs) + 7 "
+                               "product launches, eager on one stream",
+                       "tokens_per_s": "M * steps / seconds (a token goes through all seven linears)"},
             "int_tops": r["int_tops"],
-            "roofline": {"bound": "hbm", "achieved": r["gemm_gbs"], "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": r["gemm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gemm_decode_kernel<8,true,4,0>", "launch_us": r["gemm_us"],
-                         "launch_us_median": r["gemm_us_median"],
-                         "algorithmic_bytes_per_launch": r["gemm_bytes"]},
-            "quant_kernel_us": r["quant_us"],
-            "decode_sequential": sequential,
-            "decode_other_M": others,
+            "roofline": {"bound": "mfma", "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                         "frac": tops / INT8_PEAK_TOPS,
+                         "traffic": recorded_traffic("gemm_tern4_kernel", "block"),
+                         "kernel": "gemm_tern4_kernel<true,0>", "launch_us": k2_us,
+                         "launches_per_step": launches,
+                         "algorithmic_ops_per_launch": ops_launch,
+                         "timed_as": "HIP events on the launch stream around every product "
+                                     "launch of the timed steps; achieved = the step's 2*M*N*K "
+                                     "over the launches' summed durations"},
+            "end_to_end_roofline_frac": r["end_to_end_roofline_frac"],
+            "quant_share": r["quant_share"],
+            "linears": r["linears"],
             "cpu_baseline": cpu,
-            "cpu_baseline_1thread": cpu1,
         }
-        del d
         torch.cuda.empty_cache()
 
-    if not args.no_large and args.only in (None, "wo", "wdown", "block", "block_fused"):
+    if args.only in (None, "decode", "decode_grouped"):
+        dec = decode_report(torch, tb, si, args)
+        if result:
+            result["decode"] = dec
+        else:
+            g = dec["grouped"]
+            result = {"metric": METRIC, "value": g["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": g["ms_per_step"],
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "int8", "data": "synthetic", "config": {"workload": g["workload"]},
+                      "roofline": g["roofline"], "decode": dec}
+
+    if not args.no_large and args.only in (None, "wo", "wdown", "block_fused"):
         large = {}
-        for name, cfg in (("wo", 3), ("wdown", 4), ("block", 5), ("block_fused", 5)):
+        for name, cfg in (("wo", 3), ("wdown", 4), ("block_fused", 5)):
             if args.only not in (None, name):
                 continue
             log(f"[bench] {name}: preparing")
@@ -878,26 +976,15 @@ def main():
                 r = run_block_fused(torch, tb, si, args.large_steps, 2)
             else:
                 r = run_large(torch, tb, si, cfg, args.large_steps, 2)
-                if not args.no_cpu_baseline:
+                if not args.no_cpu_baseline and args.only is None:
                     import oracle
-                    r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg)
+                    r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg, rows_max=128 if cfg == 4 else 256)
                     log(f"[bench] {name}: cpu oracle {r['cpu_baseline']['value']:.4g} tokens/s "
                         f"({r['cpu_baseline']['sample']})")
-                    if cfg == 3:
-                        # the same oracle on one host thread, as context
-                        nthr = oracle.num_threads()
-                        oracle.set_num_threads(1)
-                        try:
-                            r["cpu_baseline_1thread"] = cpu_baseline_large(si, oracle, cfg, rows_max=32)
-                        finally:
-                            oracle.set_num_threads(nthr)
-                        log(f"[bench] {name}: cpu oracle, one thread, "
-                            f"{r['cpu_baseline_1thread']['value']:.4g} tokens/s "
-                            f"({r['cpu_baseline_1thread']['sample']})")
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r
-        if args.only in (None, "block_fused"):
+        if args.only is None:
             log("[bench] activation stage with the RMS norm folded in")
             large["k1_rmsnorm"] = run_k1_rmsnorm(torch, tb, si, 20)
             for nm, v in large["k1_rmsnorm"].items():
@@ -911,6 +998,27 @@ def main():
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                       "dtype": "int8", "data": "synthetic", "config": {"workload": r["workload"]},
                       "large_m": large}
+
+    if args.only in (None, "tiny"):
+        t = run_tiny(torch, tb, si)
+        if not args.no_cpu_baseline:
+            import oracle
+            t["cpu_baseline"] = cpu_baseline_tiny(si, oracle)
+            nthr = oracle.num_threads()
+            oracle.set_num_threads(1)
+            try:
+                t["cpu_baseline_1thread"] = cpu_baseline_tiny(si, oracle, min_seconds=2.0)
+            finally:
+                oracle.set_num_threads(nthr)
+        log(f"[bench] tiny: forward {t['forward_us']:.1f} us")
+        if result:
+            result["tiny"] = t
+        else:
+            result = {"metric": METRIC, "value": t["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                      "steps": 50, "warmup": 5, "ms_per_step": t["forward_us"] / 1e3,
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "int8", "data": "synthetic", "config": {"workload": t["workload"]},
+                      "tiny": t}
     print(json.dumps(result), flush=True)
 
 

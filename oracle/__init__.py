@@ -79,6 +79,10 @@ def lib():
         L.bitnet_ref_swiglu.argtypes = [P, P, I64, P]; L.bitnet_ref_swiglu.restype = None
         L.bitnet_ref_forward_swiglu.argtypes = [P, I, I, I, I, I, P, F, P, F, P]
         L.bitnet_ref_forward_swiglu.restype = I
+        L.bitnet_ref_quantize_states.argtypes = [P, I, I, I, P, P, I, P, P]
+        L.bitnet_ref_quantize_states.restype = None
+        L.bitnet_ref_forward_qkv_states.argtypes = [P, I, I, I, P, I, I, P, P, P, I, P, P]
+        L.bitnet_ref_forward_qkv_states.restype = I
         L.bitnet_ref_num_threads.argtypes = []; L.bitnet_ref_num_threads.restype = I
         L.bitnet_ref_set_num_threads.argtypes = [I]; L.bitnet_ref_set_num_threads.restype = None
         _lib = L
@@ -349,6 +353,42 @@ def forward_swiglu(x, packed_gate, gamma_gate, packed_up, gamma_up, F: int, bits
     if rc != 0:
         raise ValueError("packed buffer does not decode")
     return h
+
+
+def quantize_states(y, seg_n, bits, group: int):
+    """Low-bit Q/K/V states: y (M x sum(seg_n) fp32) -> (codes int8 M x Ntot, scales fp32
+    M x Ntot/group), absmax per token and per group of `group` columns, bits[s] per segment."""
+    y = _c(y, np.float32)
+    M, ntot = y.shape
+    n = np.asarray(seg_n, np.int32)
+    b = np.asarray(bits, np.int32)
+    assert n.size == b.size and int(n.sum()) == ntot and np.all(n % group == 0)
+    codes = np.empty((M, ntot), np.int8)
+    scales = np.empty((M, ntot // group), np.float32)
+    lib().bitnet_ref_quantize_states(_p(y), M, ntot, n.size, _p(n), _p(b), group, _p(codes),
+                                     _p(scales))
+    return codes, scales
+
+
+def forward_qkv_states(x, packs, gammas, seg_n, act_bits: int, use_hadamard: bool, bits, group: int):
+    """forward_segments, then quantize_states of its output -> (codes, scales)."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    S = len(seg_n)
+    bufs = [_c(p, np.uint8) for p in packs]
+    ptrs = (ctypes.c_void_p * S)(*[q.ctypes.data for q in bufs])
+    n = np.asarray(seg_n, np.int32)
+    g = np.asarray(gammas, np.float32)
+    b = np.asarray(bits, np.int32)
+    ntot = int(n.sum())
+    codes = np.empty((M, ntot), np.int8)
+    scales = np.empty((M, ntot // group), np.float32)
+    rc = lib().bitnet_ref_forward_qkv_states(_p(x), M, K, S, _p(n), act_bits, int(bool(use_hadamard)),
+                                             ctypes.cast(ptrs, ctypes.c_void_p), _p(g), _p(b), group,
+                                             _p(codes), _p(scales))
+    if rc != 0:
+        raise ValueError("packed buffer does not decode")
+    return codes, scales
 
 
 def num_threads() -> int:

@@ -449,6 +449,52 @@ int bitnet_ref_forward_swiglu(const float *x, int M, int K, int F, int bits, int
     return rc;
 }
 
+/* ------------------------------------------------------------------------------------- */
+/* Low-bit Q/K/V states [v2-news: the QKV states of the attention are kept at a reduced bit  */
+/* width (zero-shot tables 2 and 3, a8 and a4, QKV-state widths varied), and a 3-bit KV      */
+/* cache matches a full-precision one].  The page gives no quantiser.  Reading taken: the     */
+/* layer's own absmax rule, applied to the fp32 outputs y of the Q, K and V projections per  */
+/* token and per group of `group` consecutive output columns (one attention head):           */
+/*   gamma = max |y| over the group;  Qp = 2^(b-1) - 1 with b the segment's bit width;        */
+/*   q = clamp(rne(y * (Qp / gamma)), -Qp-1, Qp) (fp32 division, then a multiply);           */
+/*   scale = gamma / Qp;  a group of zeros gives codes 0 and scale 0.                          */
+/* y is M x Ntot with the segments side by side (Ntot = sum seg_n); `group` divides every    */
+/* seg_n.  codes: M x Ntot int8 (one code per byte); scales: M x (Ntot / group) fp32, group j  */
+/* of row m at m * (Ntot / group) + j.                                                         */
+/* ------------------------------------------------------------------------------------- */
+void bitnet_ref_quantize_states(const float *y, int M, int Ntot, int S, const int *seg_n,
+                                const int *bits, int group, int8_t *codes, float *scales)
+{
+    const int ngroups = Ntot / group;
+    for (int m = 0; m < M; m++) {
+        int col = 0;
+        for (int s = 0; s < S; s++) {
+            for (int c = col; c < col + seg_n[s]; c += group) {
+                const int64_t off = (int64_t)m * Ntot + c;
+                bitnet_ref_quantize_row(y + off, group, bits[s], codes + off,
+                                        &scales[(int64_t)m * ngroups + c / group]);
+            }
+            col += seg_n[s];
+        }
+    }
+}
+
+/* The projections and their states in one: bitnet_ref_forward_segments, then               */
+/* bitnet_ref_quantize_states of its output.                                                 */
+int bitnet_ref_forward_qkv_states(const float *x, int M, int K, int S, const int *seg_n,
+                                  int act_bits, int use_hadamard, const uint8_t *const *packed,
+                                  const float *gammas, const int *bits, int group, int8_t *codes,
+                                  float *scales)
+{
+    int ntot = 0;
+    for (int s = 0; s < S; s++) ntot += seg_n[s];
+    float *y = (float *)malloc(sizeof(float) * (size_t)M * (size_t)ntot);
+    int rc = bitnet_ref_forward_segments(x, M, K, S, seg_n, act_bits, use_hadamard, packed, gammas, y);
+    if (rc == 0) bitnet_ref_quantize_states(y, M, ntot, S, seg_n, bits, group, codes, scales);
+    free(y);
+    return rc;
+}
+
 /* Number of OpenMP threads a parallel region here uses (1 without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -567,3 +567,99 @@ def test_pack_weights_hadamard_is_rotate_then_pack():
     t = oracle.unpack(oracle.pack_weights_hadamard(Wr)[0], 16, K)
     for n in range(16):
         assert np.count_nonzero(t[n]) == 1 and t[n, 3 * n + 1] == 1
+
+
+# ------------------------------------------------------------ low-bit Q/K/V states ----
+
+def _nearest_in_range(v, qp):
+    """Brute force: the integer in [-qp-1, qp] nearest to v, ties to the even one."""
+    cands = np.arange(-qp - 1, qp + 1)
+    d = np.abs(cands - float(v))
+    best = cands[d == d.min()]
+    return int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+
+
+@pytest.mark.parametrize("b", [3, 4, 8])
+def test_states_integer_grid_is_lossless(b):
+    # a group on the integer grid whose largest magnitude is Qp: inv = 1, scale = 1, q = y
+    qp = 2 ** (b - 1) - 1
+    rng = np.random.default_rng(b)
+    group = 32
+    y = rng.integers(-qp, qp + 1, size=(5, 3 * group)).astype(np.float32)
+    y[:, ::group] = qp
+    codes, scales = oracle.quantize_states(y, [group, 2 * group], [b, b], group)
+    assert np.array_equal(codes, y.astype(np.int8))
+    assert np.all(scales == 1.0)
+
+
+@pytest.mark.parametrize("bits", [(3, 3, 3), (4, 3, 3), (8, 3, 3)])
+def test_states_group_max_bound_and_brute_force(bits):
+    seg_n, group = [128, 128, 256], 64
+    rng = np.random.default_rng(sum(bits))
+    y = (rng.standard_normal((6, 512)) * rng.uniform(0.1, 30, size=(6, 1))).astype(np.float32)
+    y[2, 128:192] = 0.0                       # one all-zero group: codes 0, scale 0
+    codes, scales = oracle.quantize_states(y, seg_n, bits, group)
+    seg_of_col = np.repeat(np.arange(3), seg_n)
+    for m in range(6):
+        for j in range(512 // group):
+            cols = slice(j * group, (j + 1) * group)
+            qp = 2 ** (bits[seg_of_col[j * group]] - 1) - 1
+            g = np.float32(np.max(np.abs(y[m, cols])))
+            q, s = codes[m, cols].astype(np.int64), scales[m, j]
+            if g == 0:
+                assert not np.any(q) and s == 0.0
+                continue
+            # the group's largest magnitude lands on +-Qp; -Qp-1 is never used; the scale is
+            # gamma / Qp
+            k = int(np.argmax(np.abs(y[m, cols])))
+            assert abs(q[k]) == qp and q.min() >= -qp
+            assert s == np.float32(g / np.float32(qp))
+            # each code is the in-range integer nearest to y * (Qp / gamma), found by search
+            inv = np.float32(qp) / g
+            for i in range(0, group, 7):
+                assert q[i] == _nearest_in_range(np.float32(y[m, j * group + i] * inv), qp)
+            # and dequantises within half a step
+            assert np.all(np.abs(y[m, cols].astype(np.float64) - s * q) <= 0.5 * s * (1 + 1e-6))
+
+
+def test_states_groups_are_independent_and_scale_exactly():
+    group = 16
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((3, 96)).astype(np.float32)
+    c0, s0 = oracle.quantize_states(y, [32, 64], [3, 4], group)
+    y2 = y.copy()
+    y2[:, 16:32] *= np.float32(8.0)           # a power of two: codes kept, scale x8 exactly
+    y2[:, 64:80] = rng.standard_normal((3, 16)).astype(np.float32)   # another group replaced
+    c2, s2 = oracle.quantize_states(y2, [32, 64], [3, 4], group)
+    assert np.array_equal(c2[:, 16:32], c0[:, 16:32]) and np.array_equal(s2[:, 1], 8 * s0[:, 1])
+    keep = np.r_[0:16, 32:64, 80:96]
+    assert np.array_equal(c2[:, keep], c0[:, keep])
+    assert np.array_equal(s2[:, [0, 2, 3, 5]], s0[:, [0, 2, 3, 5]])
+
+
+def test_forward_qkv_states_hadamard_row_closed_form():
+    # x = a * H[j, :]: each projection's output is a sqrt(K) t_s[n, j] gamma_s (values 0 and
+    # +-gamma), so every group that holds a non-zero trit quantises to q = sign(a) Qp t_s[n, j]
+    # with scale |a| sqrt(K) gamma_s / Qp; a group of zero trits gives codes 0, scale 0
+    K, group = 512, 32
+    seg_n, bits = [64, 32, 96], [4, 3, 3]
+    H = oracle.fwht(np.eye(K, dtype=np.float32))
+    packs, gammas, ts = [], [], []
+    for s, n in enumerate(seg_n):
+        p, g, t = oracle.pack_weights(si.gaussian_weights(13, n, K, layer=s, std=0.01 * (s + 1)))
+        packs.append(p); gammas.append(g); ts.append(t)
+    for j, a in ((3, 1.25), (K - 2, -0.5)):
+        x = (np.float32(a) * H[j])[None, :]
+        codes, scales = oracle.forward_qkv_states(x, packs, gammas, seg_n, 4, True, bits, group)
+        col = 0
+        for s, n in enumerate(seg_n):
+            qp = 2 ** (bits[s] - 1) - 1
+            tj = ts[s][:, j].astype(np.int64)
+            assert np.array_equal(codes[0, col:col + n], (np.sign(a) * qp * tj).astype(np.int8))
+            for gi in range(n // group):
+                sc = scales[0, (col + gi * group) // group]
+                if np.any(tj[gi * group:(gi + 1) * group]):
+                    assert sc == pytest.approx(abs(a) * math.sqrt(K) * float(gammas[s]) / qp, rel=1e-6)
+                else:
+                    assert sc == 0.0
+            col += n
