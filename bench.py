@@ -43,7 +43,7 @@ def parse_args():
     p.add_argument("--no-large", action="store_true", help="skip the large-M workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["headline", "decode", "decode_grouped", "wo", "wdown",
-                                      "block_fused", "tiny"],
+                                      "block_fused", "qkv_states", "tiny"],
                    default=None,
                    help="run one workload only (profiling): 'headline' is the 7B block alone; "
                         "'decode_grouped' the grouped M = --M decode launch alone")
@@ -728,6 +728,56 @@ def run_block_fused(torch, tb, si, steps, warmup):
     return res
 
 
+def run_qkv_states(torch, tb, si, steps):
+    """The block's Q, K and V projections (M = 16384, K = 4096, one three-segment product launch
+    on one activation stage) with the low-bit states fused into the epilogue (Q 4 bits, K and V
+    3 bits, heads of 128: int8 codes and a scale per head) against the same launch writing the
+    fp32 projections."""
+    import numpy as np
+    wl = si.workload(5)
+    L = {l.name: l for l in wl.linears}
+    M, K = L["q"].M, L["q"].K
+    seg_n = [L[n].N for n in ("q", "k", "v")]
+    N = sum(seg_n)
+    bits, group = [4, 3, 3], 128
+    x = torch.from_numpy(si.activations(5, L["q"])).cuda()
+    W = np.concatenate([si.weights(5, L[n]) for n in ("q", "k", "v")])
+    packed, gs = tb.bitnet_pack_weights_segments(W, seg_n)
+    del W
+    pw = torch.from_numpy(packed).cuda()
+    codes, scales = tb.hbitlinear_quantize(x, 4, False)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    sc = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    ss = torch.empty((M, N // group), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = dict(M=M, K=K, seg_n=seg_n, state_bits=bits, group=group)
+    for mode in ("fp32", "states"):
+        def once():
+            if mode == "fp32":
+                tb.hbitlinear_gemm_dequant_segments(codes, scales, M, K, seg_n, 4, pw, gs, out=y,
+                                                    stream=stream)
+            else:
+                tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, 4, pw, gs, bits, group,
+                                              state_codes=sc, state_scales=ss, stream=stream)
+        for _ in range(2):
+            once()
+        t = Timer(torch, steps)
+        for _ in range(steps):
+            t.begin(stream)
+            once()
+            t.end(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * t.mean_ms()
+        out_bytes = 4 * M * N if mode == "fp32" else M * N + 4 * M * (N // group)
+        res[mode] = dict(launch_us=us, tops=2.0 * M * N * K / (us * 1e-6) / 1e12,
+                         output_bytes=out_bytes)
+    res.update(workload=f"bitnet_v2_qkv_states_int4_M{M}_K{K}", ms_per_step=res["states"]["launch_us"] / 1e3,
+               tokens_per_s=M / (res["states"]["launch_us"] * 1e-6))
+    del x, y, sc, ss, codes, scales
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_k1_rmsnorm(torch, tb, si, steps):
     """The activation stage with and without the RMS norm folded in, at the large-M shapes: the
     norm adds a reduction and a gain read but no pass over x."""
@@ -966,7 +1016,7 @@ def main():
                       "dtype": "int8", "data": "synthetic", "config": {"workload": g["workload"]},
                       "roofline": g["roofline"], "decode": dec}
 
-    if not args.no_large and args.only in (None, "wo", "wdown", "block_fused"):
+    if not args.no_large and args.only in (None, "wo", "wdown", "block_fused", "qkv_states"):
         large = {}
         for name, cfg in (("wo", 3), ("wdown", 4), ("block_fused", 5)):
             if args.only not in (None, name):
@@ -984,6 +1034,10 @@ def main():
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r
+        if args.only in (None, "qkv_states"):
+            large["qkv_states"] = r = run_qkv_states(torch, tb, si, args.large_steps)
+            log(f"[bench] qkv states: fp32 out {r['fp32']['launch_us']:.1f} us, states fused "
+                f"{r['states']['launch_us']:.1f} us")
         if args.only is None:
             log("[bench] activation stage with the RMS norm folded in")
             large["k1_rmsnorm"] = run_k1_rmsnorm(torch, tb, si, 20)

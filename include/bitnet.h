@@ -211,6 +211,27 @@ int hbitlinear_forward_segments(const float *x, int M, int K, int S, const int *
                                 const uint8_t *packed_w, const float *w_scales, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Low-bit Q/K/V states [v2 write-up: the attention's QKV states kept at reduced bit widths
+ * (zero-shot tables 2 and 3, with 8-bit and 4-bit activations), and a 3-bit KV cache matching
+ * a full-precision one; the page gives no quantiser, reading taken: the layer's absmax rule
+ * per token and per head]: the projections of hbitlinear_forward_segments, y (never written
+ * to memory), quantised in the product's epilogue per row and per group of `group` consecutive
+ * output columns (one head) with the segment's bit width b = state_bits[s]:
+ *   gamma = max |y| over the group;  Qp = 2^(b-1) - 1;
+ *   q = clamp(round_half_even(y * (Qp / gamma)), -Qp-1, Qp);  scale = gamma / Qp
+ *   (a group of zeros gives q = 0, scale = 0).
+ * state_codes (device): M x sum(seg_n) int8, one code per byte, row-major; state_scales
+ * (device): M x (sum(seg_n) / group) fp32, group j of row m at m * (sum seg_n / group) + j.
+ * seg_n, w_scales, state_bits are host arrays of S entries; state_bits[s] in [2, 8]; group is
+ * 64 or 128 and divides every seg_n[s].  Built for INT4 activations with M > 16 (the batched
+ * case); other act_bits or M <= 16 return BITNET_ERR_UNSUPPORTED.  Other rules, the packed
+ * weights and the workspace as hbitlinear_forward_segments. */
+int hbitlinear_forward_qkv_states(const float *x, int M, int K, int S, const int *seg_n,
+                                  int act_bits, int use_hadamard, const uint8_t *packed_w,
+                                  const float *w_scales, const int *state_bits, int group,
+                                  int8_t *state_codes, float *state_scales, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Gated feed-forward input projections with the SwishGLU glue in the product's epilogue
  * [v2 write-up: SwishGLU; reading taken: Swish with beta = 1, SiLU(z) = z / (1 + e^-z)]:
  *   g = forward(x, gate), u = forward(x, up)   (each exactly as hbitlinear_forward)
@@ -271,12 +292,17 @@ int hbitlinear_gemm_dequant_grouped(const uint8_t *codes, const float *scales, i
                                     int K, int N, int act_bits, const uint8_t *const *packed_ws,
                                     const float *w_scales, float *out, void *stream);
 
-/* The product stages of hbitlinear_forward_segments and hbitlinear_forward_swiglu, from codes
- * and scales as written by hbitlinear_quantize (device); seg_n, w_scales host arrays. */
+/* The product stages of hbitlinear_forward_segments, hbitlinear_forward_qkv_states and
+ * hbitlinear_forward_swiglu, from codes and scales as written by hbitlinear_quantize
+ * (device); seg_n, w_scales, state_bits host arrays. */
 int hbitlinear_gemm_dequant_segments(const uint8_t *codes, const float *scales, int M, int K,
                                      int S, const int *seg_n, int act_bits,
                                      const uint8_t *packed_w, const float *w_scales, float *out,
                                      void *stream);
+int hbitlinear_gemm_qkv_states(const uint8_t *codes, const float *scales, int M, int K, int S,
+                               const int *seg_n, int act_bits, const uint8_t *packed_w,
+                               const float *w_scales, const int *state_bits, int group,
+                               int8_t *state_codes, float *state_scales, void *stream);
 int hbitlinear_gemm_swiglu(const uint8_t *codes, const float *scales, int M, int K, int F,
                            int act_bits, const uint8_t *packed_gate_up, float gate_scale,
                            float up_scale, float *h, void *stream);

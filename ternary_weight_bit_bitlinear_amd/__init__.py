@@ -14,5 +14,6 @@ from .bitnet import (  # noqa: F401
     bitnet_pack_gate_up, bitnet_pack_weights_segments, hbitlinear_forward_segments,
     hbitlinear_forward_swiglu, hbitlinear_gemm_dequant_segments, hbitlinear_gemm_swiglu,
     hbitlinear_forward_rmsnorm, hbitlinear_quantize_rmsnorm, bitnet_pack_weights_hadamard,
-    hbitlinear_forward_noalloc, NOALLOC_SCRATCH_BYTES,
+    hbitlinear_forward_noalloc, NOALLOC_SCRATCH_BYTES, hbitlinear_forward_qkv_states,
+    hbitlinear_gemm_qkv_states,
 )

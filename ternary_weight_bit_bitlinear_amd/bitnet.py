@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "hbitlinear_gemm_dequant_segments": ([P, P, I, I, I, P, I, P, P, P, P], I),
             "hbitlinear_forward_swiglu": ([P, I, I, I, I, I, P, P, F, F, P, SZ, P], I),
             "hbitlinear_gemm_swiglu": ([P, P, I, I, I, I, P, F, F, P, P], I),
+            "hbitlinear_forward_qkv_states": ([P, I, I, I, P, I, I, P, P, P, I, P, P, P, SZ, P], I),
+            "hbitlinear_gemm_qkv_states": ([P, P, I, I, I, P, I, P, P, P, I, P, P, P], I),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -297,6 +299,72 @@ def hbitlinear_forward_segments(x, seg_n, act_bits: int, use_hadamard: bool, pac
                                              _ptr(g), _ptr(workspace), workspace.numel(),
                                              _stream(stream)), "hbitlinear_forward_segments")
     return out
+
+
+def _state_outputs(M, N, group, state_codes, state_scales, device):
+    import torch
+    if state_codes is None:
+        state_codes = torch.empty((M, N), dtype=torch.int8, device=device)
+    if state_scales is None:
+        state_scales = torch.empty((M, N // group), dtype=torch.float32, device=device)
+    if state_codes.numel() < M * N or state_scales.numel() < M * (N // group):
+        raise ValueError("state_codes or state_scales is too small")
+    _dev_check(state_codes, torch.int8, "state_codes")
+    _dev_check(state_scales, torch.float32, "state_scales")
+    return state_codes, state_scales
+
+
+def hbitlinear_forward_qkv_states(x, seg_n, act_bits: int, use_hadamard: bool, packed_w, w_scales,
+                                  state_bits, group: int, state_codes=None, state_scales=None,
+                                  workspace=None, stream=None):
+    """Low-bit Q/K/V states: the projections of x (M x K fp32, device) by the stacked matrices
+    of bitnet_pack_weights_segments, quantised per row and per `group` columns to
+    state_bits[s] bits -> (state_codes int8 M x N, state_scales fp32 M x N/group), device."""
+    import torch
+    n, g = _seg_arrays(seg_n, w_scales)
+    b = np.ascontiguousarray(state_bits, dtype=np.int32)
+    if b.size != n.size:
+        raise ValueError("state_bits needs one entry per segment")
+    M, K = _rows_k(x)
+    N = int(n.sum())
+    _packed_check(packed_w, N, K, "packed_w")
+    _dev_check(x, torch.float32, "x")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    state_codes, state_scales = _state_outputs(M, N, group, state_codes, state_scales, x.device)
+    if workspace is None:
+        workspace = torch.empty(hbitlinear_workspace_bytes(M, K, act_bits), dtype=torch.uint8,
+                                device=x.device)
+    _dev_check(workspace, torch.uint8, "workspace")
+    _check(lib().hbitlinear_forward_qkv_states(_ptr(x), M, K, n.size, _ptr(n), act_bits,
+                                               int(bool(use_hadamard)), _ptr(packed_w), _ptr(g),
+                                               _ptr(b), group, _ptr(state_codes), _ptr(state_scales),
+                                               _ptr(workspace), workspace.numel(), _stream(stream)),
+           "hbitlinear_forward_qkv_states")
+    return state_codes, state_scales
+
+
+def hbitlinear_gemm_qkv_states(codes, scales, M: int, K: int, seg_n, act_bits: int, packed_w,
+                               w_scales, state_bits, group: int, state_codes=None,
+                               state_scales=None, stream=None):
+    """Product stage of hbitlinear_forward_qkv_states from device codes and scales."""
+    import torch
+    n, g = _seg_arrays(seg_n, w_scales)
+    b = np.ascontiguousarray(state_bits, dtype=np.int32)
+    if b.size != n.size:
+        raise ValueError("state_bits needs one entry per segment")
+    N = int(n.sum())
+    _packed_check(packed_w, N, K, "packed_w")
+    if codes.numel() < hbitlinear_codes_bytes(M, K, act_bits) or scales.numel() < M:
+        raise ValueError("codes or scales buffer is too small")
+    _dev_check(codes, torch.uint8, "codes")
+    _dev_check(scales, torch.float32, "scales")
+    _dev_check(packed_w, torch.uint8, "packed_w")
+    state_codes, state_scales = _state_outputs(M, N, group, state_codes, state_scales, codes.device)
+    _check(lib().hbitlinear_gemm_qkv_states(_ptr(codes), _ptr(scales), M, K, n.size, _ptr(n),
+                                            act_bits, _ptr(packed_w), _ptr(g), _ptr(b), group,
+                                            _ptr(state_codes), _ptr(state_scales), _stream(stream)),
+           "hbitlinear_gemm_qkv_states")
+    return state_codes, state_scales
 
 
 def hbitlinear_forward_swiglu(x, F: int, act_bits: int, use_hadamard: bool, packed_gate_up,

@@ -103,6 +103,28 @@ int segment_form(int S, const int* seg_n, const float* w_scales, int* n_total, O
     return BITNET_OK;
 }
 
+// Low-bit states of stacked linears: the segments' form plus, per segment, the states' Qp,
+// and the group (head) size.  Built for the INT4 large-M product kernel (act_bits 4, M > 16),
+// whose wave tile of 128 columns holds whole groups of 64 or 128.
+int states_form(int S, const int* seg_n, const float* w_scales, const int* state_bits, int group,
+                int M, int act_bits, float* state_scales, int* n_total, OutForm* of)
+{
+    int rc = segment_form(S, seg_n, w_scales, n_total, of);
+    if (rc != BITNET_OK) return rc;
+    if (state_bits == nullptr || state_scales == nullptr) return BITNET_ERR_NULL;
+    if (group != 64 && group != 128) return BITNET_ERR_UNSUPPORTED;
+    for (int s = 0; s < S; s++) {
+        if (seg_n[s] % group != 0) return BITNET_ERR_UNSUPPORTED;
+        if (state_bits[s] < 2 || state_bits[s] > 8) return BITNET_ERR_UNSUPPORTED;
+        of->seg_qp[s] = (1 << (state_bits[s] - 1)) - 1;
+    }
+    if (act_bits != 4 || M <= 16) return BITNET_ERR_UNSUPPORTED;
+    of->states = 1;
+    of->state_tiles = group / 16;
+    of->state_scales = state_scales;
+    return BITNET_OK;
+}
+
 // Gate / up pairs of F rows each (F % 16 == 0): 2F weight rows, M x F output.
 int glu_form(int F, float gate_scale, float up_scale, OutForm* of)
 {
@@ -297,6 +319,48 @@ int hbitlinear_forward_segments(const float* x, int M, int K, int S, const int* 
     if (e != hipSuccess) return BITNET_ERR_HIP;
     return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
                                  0.0f, out, nullptr, s, of));
+}
+
+int hbitlinear_gemm_qkv_states(const uint8_t* codes, const float* scales, int M, int K, int S,
+                               const int* seg_n, int act_bits, const uint8_t* packed_w,
+                               const float* w_scales, const int* state_bits, int group,
+                               int8_t* state_codes, float* state_scales, void* stream)
+{
+    if (codes == nullptr || scales == nullptr || packed_w == nullptr || state_codes == nullptr)
+        return BITNET_ERR_NULL;
+    OutForm of;
+    int N = 0;
+    int rc = states_form(S, seg_n, w_scales, state_bits, group, M, act_bits, state_scales, &N, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, N, act_bits, 0);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 0.0f, reinterpret_cast<float*>(state_codes), nullptr,
+                                 (hipStream_t)stream, of));
+}
+
+int hbitlinear_forward_qkv_states(const float* x, int M, int K, int S, const int* seg_n,
+                                  int act_bits, int use_hadamard, const uint8_t* packed_w,
+                                  const float* w_scales, const int* state_bits, int group,
+                                  int8_t* state_codes, float* state_scales, void* workspace,
+                                  size_t workspace_size, void* stream)
+{
+    if (x == nullptr || packed_w == nullptr || state_codes == nullptr) return BITNET_ERR_NULL;
+    OutForm of;
+    int N = 0;
+    int rc = states_form(S, seg_n, w_scales, state_bits, group, M, act_bits, state_scales, &N, &of);
+    if (rc == BITNET_OK) rc = check_shape(M, K, N, act_bits, use_hadamard);
+    if (rc == BITNET_OK) rc = check_gemm_limits(M, K, N, act_bits);
+    if (rc != BITNET_OK) return rc;
+    if (workspace == nullptr || workspace_size < workspace_bytes(M, K, act_bits))
+        return BITNET_ERR_WORKSPACE;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + align256(codes_bytes(M, K, act_bits)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize(x, M, K, act_bits, use_hadamard, codes, scales, nullptr, s);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+    return status_of(launch_gemm(codes, 1, M, K, N, act_bits, nullptr, packed_w, scales, nullptr,
+                                 0.0f, reinterpret_cast<float*>(state_codes), nullptr, s, of));
 }
 
 int hbitlinear_gemm_swiglu(const uint8_t* codes, const float* scales, int M, int K, int F,

@@ -31,7 +31,11 @@ int device_cus();
 //  - glu: a gate matrix and an up matrix of F rows each, interleaved by 16-row groups (group
 //    2i = gate rows 16i..16i+15, group 2i+1 = the same up rows); the output is M x F,
 //    h = SiLU(gate) * up, each of gate and up dequantised with its own weight scale.
-// The default (nseg = 0, glu = 0) is the plain epilogue.
+//  - states (with segments): every dequantised output is quantised again, per row and per
+//    group of 16 * state_tiles consecutive columns (an attention head), to its segment's
+//    seg_qp[s] = 2^(b-1) - 1; the output is the int8 codes (M x N), and state_scales (M x
+//    N / (16 * state_tiles) fp32) receives gamma / Qp per group.
+// The default (nseg = 0, glu = 0, states = 0) is the plain epilogue.
 constexpr int kMaxSegments = 8;
 struct OutForm {
     int nseg = 0;
@@ -39,6 +43,10 @@ struct OutForm {
     float seg_scale[kMaxSegments] = {};
     int glu = 0;
     float gate_scale = 0.0f, up_scale = 0.0f;
+    int states = 0;
+    int state_tiles = 0;
+    int seg_qp[kMaxSegments] = {};
+    float* state_scales = nullptr;
 };
 
 // Weight scale of 16-row group grp: its segment's scale, or dflt without segments.
@@ -49,6 +57,15 @@ __host__ __device__ inline float group_scale(const OutForm& of, int grp, float d
     for (int i = 1; i < kMaxSegments; i++)
         if (i < of.nseg && grp >= of.seg_end[i - 1]) s = of.seg_scale[i];
     return s;
+}
+
+// Qp of the states of 16-row group grp: its segment's seg_qp.
+__host__ __device__ inline int group_qp(const OutForm& of, int grp)
+{
+    int q = of.seg_qp[0];
+    for (int i = 1; i < kMaxSegments; i++)
+        if (i < of.nseg && grp >= of.seg_end[i - 1]) q = of.seg_qp[i];
+    return q;
 }
 
 // SiLU(g) * u in fp32, SiLU(z) = z / (1 + e^-z), with the hardware exp2 and reciprocal:

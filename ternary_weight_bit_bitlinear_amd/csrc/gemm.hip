@@ -202,6 +202,87 @@ __device__ __forceinline__ void store_tiles_glu(const v4i (&acc)[FM][FN], int ro
     }
 }
 
+// Maximum over the 16 lanes 16 i .. 16 i + 15 that share this lane's MFMA output rows, by
+// DPP moves inside the row of 16 lanes: swap neighbours, swap pairs, mirror the halves of
+// eight, mirror the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+    return v;
+}
+
+// Low-bit Q/K/V states (BitNet v2 write-up: QKV states at reduced bit widths, zero-shot
+// tables 2 and 3; a 3-bit KV cache): each output y, dequantised as in store_tiles, is
+// quantised per row and per group of 16 TG consecutive columns (one attention head) with its
+// segment's Qp: gamma = max |y| over the group, q = clamp(rne(y * (Qp / gamma)), -Qp-1, Qp)
+// (IEEE division), scale = gamma / Qp, a zero group giving codes 0 and scale 0.  The group's
+// columns are this wave's tiles TG j .. TG j + TG - 1 of one row, held by the 16 lanes of the
+// row's lane group, so the maximum runs over TG registers and then max16.  Codes go out as
+// bytes (M x N int8 at cbase), scales as M x N / (16 TG) fp32.  Offsets outside the outputs
+// are dropped by the buffer range, as in store_tiles.
+template <int FM, int FN, int SHIFT, int TG, typename ScaleFn, typename WScaleFn>
+__device__ __forceinline__ void store_tiles_states(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
+                                                   int M, int N, ScaleFn sxf, WScaleFn wsf,
+                                                   const OutForm& of, void* cbase)
+{
+    static_assert(FN % TG == 0, "a group is whole tiles of the wave");
+    constexpr int NG = FN / TG;
+    const int g = lane >> 4;
+    const auto crs = __builtin_amdgcn_make_buffer_rsrc(cbase, 0, 0x7FFFFFFF, 0x00020000);
+    const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)of.state_scales, 0, 0x7FFFFFFF, 0x00020000);
+    const int ngroups = N / (16 * TG);
+    float wsv[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+        wsv[fn] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsf(fn))));
+    int qpv[NG];
+#pragma unroll
+    for (int j = 0; j < NG; j++) qpv[j] = __builtin_amdgcn_readfirstlane(group_qp(of, col0 / 16 + TG * j));
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = row0 + 16 * fm + 4 * g + r;
+            float y[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++) y[fn] = ((float)(acc[fm][fn][r] >> SHIFT) * sx[r]) * wsv[fn];
+#pragma unroll
+            for (int j = 0; j < NG; j++) {
+                float a = 0.0f;
+#pragma unroll
+                for (int t = 0; t < TG; t++) a = fmaxf(a, fabsf(y[TG * j + t]));
+                a = max16(a);
+                const int qp = qpv[j];
+                const float inv = a > 0.0f ? (float)qp / a : 0.0f;   // IEEE division
+#pragma unroll
+                for (int t = 0; t < TG; t++) {
+                    const int fn = TG * j + t;
+                    const int col = col0 + 16 * fn + (lane & 15);
+                    int q = (int)__builtin_rintf(y[fn] * inv);        // round half to even
+                    q = q > qp ? qp : (q < -qp - 1 ? -qp - 1 : q);
+                    const uint32_t off = (row < M && col < N) ? (uint32_t)(row * N + col) : 0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q, crs, (int)off, 0, 0);
+                }
+                const int grp = (col0 + 16 * TG * j) / (16 * TG);
+                const float sc = a > 0.0f ? a / (float)qp : 0.0f;
+                const uint32_t soff = (row < M && grp < ngroups && (lane & 15) == 0)
+                                          ? 4u * (uint32_t)(row * ngroups + grp) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), srs, (int)soff, 0, 0);
+            }
+        }
+    }
+}
+
 // Nibbles (two's complement) in the low half of each byte -> int8 in each byte:
 // ((n ^ 8) + 0x78) ^ 0x80 stays within the byte, so four lanes go at once.
 __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
@@ -211,7 +292,7 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
 
 // Epilogue forms, one instantiation each (the plain one carries none of the others' code):
 // one weight scale per layer; a scale per row segment; gate / up pairs.
-enum Epi { kPlain = 0, kSegments = 1, kGlu = 2 };
+enum Epi { kPlain = 0, kSegments = 1, kGlu = 2, kStates = 3 };
 
 template <int BITS, bool DEQ, int EPI>
 __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
@@ -395,7 +476,7 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
 }
 
 
-template <bool DEQ, int EPI>
+template <bool DEQ, int EPI, int SG = 0>
 __global__ __launch_bounds__(NT4) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tern4_kernel(LargeArgs args)
 {
@@ -632,6 +713,11 @@ void gemm_tern4_kernel(LargeArgs args)
     if constexpr (EPI == kGlu)
         store_tiles_glu<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, M, N / 2, sxf, args.of.gate_scale,
                                  args.of.up_scale, obase);
+    else if constexpr (EPI == kStates)
+        store_tiles_states<8, 8, 4, SG>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
+                                        [&](int fn) __attribute__((always_inline)) {
+                                            return group_scale(args.of, n0 / 16 + fn, w_scale);
+                                        }, args.of, (void*)args.out);
     else if constexpr (EPI == kSegments)
         store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
                                   [&](int fn) __attribute__((always_inline)) {
@@ -658,9 +744,14 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N, of};
+    if (of.states && (bits != 4 || L != 1 || out_f32 == nullptr || of.nseg == 0 ||
+                      (of.state_tiles != 4 && of.state_tiles != 8) || N % (16 * of.state_tiles) != 0))
+        return hipErrorInvalidValue;
     if (bits == 4) {
         dim3 grid((N + BN4 - 1) / BN4, (M + BM4 - 1) / BM4, L);
-        if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);
+        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 8>), grid, dim3(NT4), 0, stream, a);
+        else if (of.states) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 4>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);
         else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4_kernel<true, kSegments>), grid, dim3(NT4), 0, stream, a);
         else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4_kernel<true, kPlain>), grid, dim3(NT4), 0, stream, a);
         else hipLaunchKernelGGL((gemm_tern4_kernel<false, kPlain>), grid, dim3(NT4), 0, stream, a);
@@ -679,6 +770,7 @@ hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bit
                        const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
                        hipStream_t stream, const OutForm& of)
 {
+    if (of.states && M <= 16) return hipErrorInvalidValue;   // the decode kernels have no states form
     if (M <= 16)
         return launch_gemm_decode(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
                                   out_f32, acc_i32, stream, of);

@@ -338,3 +338,26 @@ def test_noalloc_validation_without_launch():
     assert L.hbitlinear_forward_noalloc(FAKE, 4096, 4096, 64, 8, 0, FAKE, FAKE, f, NUL) == \
         tb.BITNET_ERR_WORKSPACE
     assert tb.hbitlinear_workspace_bytes(4096, 4096, 4) <= tb.NOALLOC_SCRATCH_BYTES
+
+
+def test_qkv_states_validation():
+    L = tb.lib()
+    n3 = (ctypes.c_int * 3)(128, 128, 128)
+    w3 = (ctypes.c_float * 3)(1.0, 1.0, 1.0)
+    b3 = (ctypes.c_int * 3)(4, 3, 3)
+    bad_b = (ctypes.c_int * 3)(4, 1, 3)
+    odd = (ctypes.c_int * 3)(128, 64, 128)
+    args = lambda M=4096, K=4096, S=3, n=n3, act=4, bits=b3, grp=128, sc=FAKE, ws=1 << 30: (
+        FAKE, M, K, S, n, act, 0, FAKE, w3, bits, grp, FAKE, sc, FAKE, ws, NUL)
+    f = L.hbitlinear_forward_qkv_states
+    assert f(*args(sc=NUL)) == tb.BITNET_ERR_NULL
+    assert f(*args(grp=32)) == tb.BITNET_ERR_UNSUPPORTED             # group 64 or 128
+    assert f(*args(n=odd)) == tb.BITNET_ERR_UNSUPPORTED              # 64 rows: not whole groups
+    assert f(*args(bits=bad_b)) == tb.BITNET_ERR_UNSUPPORTED         # 1-bit states
+    assert f(*args(act=8)) == tb.BITNET_ERR_UNSUPPORTED              # INT4 activations only
+    assert f(*args(M=16)) == tb.BITNET_ERR_UNSUPPORTED               # batched shapes only
+    assert f(*args(ws=16)) == tb.BITNET_ERR_WORKSPACE
+    g = L.hbitlinear_gemm_qkv_states
+    assert g(FAKE, FAKE, 4096, 4096, 3, n3, 4, FAKE, w3, b3, 128, NUL, FAKE, NUL) == tb.BITNET_ERR_NULL
+    assert g(FAKE, FAKE, 16, 4096, 3, n3, 4, FAKE, w3, b3, 128, FAKE, FAKE, NUL) == \
+        tb.BITNET_ERR_UNSUPPORTED

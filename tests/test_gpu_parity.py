@@ -727,3 +727,85 @@ def test_weight_activation_hadamard_variant(tb):
     e_rot = np.linalg.norm(y1.cpu().numpy() - r1) / np.linalg.norm(r1)
     say(f"  INT4 activation-quantisation error: rotated {e_rot:.4f}, plain {e_plain:.4f}")
     assert e_rot < 0.75 * e_plain
+
+
+# ------------------------------------------------------------- low-bit Q/K/V states ----
+
+def _states_reference(q_rows, s_rows, ts, gs, seg_n, bits, group):
+    """The oracle's product and epilogue on the given codes, then its state quantiser."""
+    y = np.concatenate([oracle.epilogue(oracle.gemm(q_rows, t), s_rows, np.float32(g))
+                        for t, g in zip(ts, gs)], axis=1)
+    return oracle.quantize_states(y, seg_n, bits, group)
+
+
+# The states form of the INT4 large-M kernel: segment boundaries inside a 128-column tile
+# (groups of 64), ragged M, Q at 4 or 8 bits with K and V at 3; every row and column against
+# the oracle run on the GPU's own activation codes (bit-identical codes and scales), and the
+# whole call against the oracle's forward on rows whose activation codes agree.
+@pytest.mark.parametrize("M,K,seg_n,bits,group,had", [
+    (300, 2048, [256, 128, 128], [4, 3, 3], 128, False),
+    (17, 512, [128, 64, 192], [8, 3, 3], 64, True),
+    (600, 4096, [512, 512, 512], [4, 3, 3], 128, True),
+])
+def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had):
+    say(f"  qkv states M={M} K={K} seg_n={seg_n} bits={bits} group={group} had={had}")
+    x = si.wo_activations(M, K) if had else si.normal(si.seed_for(9, 5) + M, M * K).reshape(M, K)
+    x[M // 3] = 0.0                                   # a zero row: every group zero
+    Ws = [si.gaussian_weights(9, n, K, layer=30 + s, std=0.01 * (s + 1)) for s, n in enumerate(seg_n)]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    ots = [oracle.ternarize(W) for W in Ws]
+    assert np.array_equal(np.asarray(gs, np.float32), np.array([g for _, g in ots], np.float32))
+    pw = dev(packed)
+    codes, scales, q, s = _gpu_codes(tb, x, 4, had)
+    sc, ss = tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, 4, pw, gs, bits, group)
+    fc, fs = tb.hbitlinear_forward_qkv_states(dev(x), seg_n, 4, had, pw, gs, bits, group)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, fc) and torch.equal(ss, fs)
+    ec, es = _states_reference(q, s, [t for t, _ in ots], gs, seg_n, bits, group)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ec)
+    np.testing.assert_array_equal(ss.cpu().numpy(), es)
+    assert np.all(sc.cpu().numpy()[M // 3] == 0) and np.all(ss.cpu().numpy()[M // 3] == 0)
+    # 3-bit states use the codes -3..3 only
+    col = np.cumsum([0] + seg_n)
+    for sgi, b in enumerate(bits):
+        part = sc.cpu().numpy()[:, col[sgi]:col[sgi + 1]]
+        assert part.min() >= -(2 ** (b - 1) - 1) and part.max() <= 2 ** (b - 1) - 1
+    # end to end against the oracle's own activation stage
+    oc, os_ = oracle.forward_qkv_states(x, [oracle.pack(t) for t, _ in ots], gs, seg_n, 4, had, bits, group)
+    oq, _ = oracle.quantize(x, 4, had)
+    match = np.all(oq == q, axis=1)
+    assert match.mean() > 0.9
+    np.testing.assert_array_equal(sc.cpu().numpy()[match], oc[match])
+    np.testing.assert_array_equal(ss.cpu().numpy()[match], os_[match])
+
+
+# The block's Q, K and V at full size (M = 16384, K = 4096, three 4096-row segments), launched
+# with the states fused as the benchmark does: Q at 4 bits, K and V at 3, heads of 128; one
+# sampled row in every 512-row tile of the kernel plus the whole last tile's first and last
+# rows, against the oracle on the GPU's codes.
+def test_qkv_states_full_size(tb):
+    wl = si.workload(5)
+    L = {l.name: l for l in wl.linears}
+    M, K = L["q"].M, L["q"].K
+    seg_n = [L[n].N for n in ("q", "k", "v")]
+    bits, group = [4, 3, 3], 128
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([np.arange(0, M, 512) + rng.integers(0, 512, M // 512),
+                                     [0, M - 512, M - 1]]))
+    say(f"  qkv states full size M={M}: {rows.size} rows, one in each 512-row tile")
+    x = si.activations(5, L["q"])
+    Ws = [si.weights(5, L[n]) for n in ("q", "k", "v")]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    ts = [oracle.ternarize(W)[0] for W in Ws]
+    del Ws
+    codes, scales = tb.hbitlinear_quantize(dev(x), 4, False)
+    sc, ss = tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, 4, dev(packed), gs, bits, group)
+    torch.cuda.synchronize()
+    q = codes_to_int8(codes, M, K, 4)[rows]
+    sx = scales.cpu().numpy()[rows]
+    oq, osx = oracle.quantize(x[rows], 4, False)
+    np.testing.assert_array_equal(q, oq)
+    np.testing.assert_array_equal(sx, osx)
+    ec, es = _states_reference(q, sx, ts, gs, seg_n, bits, group)
+    np.testing.assert_array_equal(sc.cpu().numpy()[rows], ec)
+    np.testing.assert_array_equal(ss.cpu().numpy()[rows], es)
