@@ -581,6 +581,12 @@ def run_large(torch, tb, si, config, steps, warmup):
 
     for _ in range(warmup):
         step()
+    # untimed steps for about 0.3 s more, so that the clocks have settled before timing
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     tq = [Timer(torch, steps) for _ in range(n)]
     tg = [Timer(torch, steps) for _ in range(n)]
     torch.cuda.synchronize()
@@ -690,6 +696,11 @@ def run_block_fused(torch, tb, si, steps, warmup):
 
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     tq = [Timer(torch, steps) for _ in names]
     tg = [Timer(torch, steps) for _ in names]
     torch.cuda.synchronize()

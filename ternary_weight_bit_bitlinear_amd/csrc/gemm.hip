@@ -103,6 +103,15 @@ __device__ __forceinline__ void block_sync()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The same barrier, but this wave's last 10 LDS operations may still be in flight.  LDS
+// operations complete in issue order, so every earlier one -- in particular every LDS write
+// the barrier publishes -- has completed.  For a caller whose last LDS write is followed by at
+// least 10 LDS reads it does not need before the barrier (the next slab's operands).
+__device__ __forceinline__ void block_sync_reads_in_flight()
+{
+    asm volatile("s_waitcnt lgkmcnt(10)\n\ts_barrier" ::: "memory");
+}
+
 // v_mfma_i32_16x16x64_i8 with the accumulator tied to one set of accumulation registers
 // (acc += a . b).  Written out because the compiler otherwise moves accumulators between
 // register sets around every MFMA.  The accumulators are read only by later MFMAs of the
@@ -167,6 +176,36 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[FM][FN], int row0, 
                     v = (uint32_t)a;
                 const uint32_t off = (row < M && col < N) ? 4u * (uint32_t)(row * N + col) : 0x80000000u;
                 __builtin_amdgcn_raw_buffer_store_b32(v, ors, (int)off, 0, 0);
+            }
+        }
+    }
+}
+
+// store_tiles for a wave tile that lies wholly inside M x N, so no output needs a bounds test:
+// the lane's offset is one VGPR, the row of (fm, r) a scalar offset and the tile column an
+// immediate offset, and each output costs its dequantisation and one store.
+template <int FM, int FN, int SHIFT, typename ScaleFn, typename WScaleFn>
+__device__ __forceinline__ void store_tiles_inside(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
+                                                   int N, ScaleFn sxf, WScaleFn wsf, float* out)
+{
+    const int g = lane >> 4;
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc((void*)(out + (int64_t)row0 * N + col0), 0,
+                                                       0x7FFFFFFF, 0x00020000);
+    float wsv[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+        wsv[fn] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsf(fn))));
+    const int voff = 4 * (4 * g * N + (lane & 15));
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int soff = __builtin_amdgcn_readfirstlane(4 * (16 * fm + r) * N);
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++) {
+                const float v = ((float)(acc[fm][fn][r] >> SHIFT) * sx[r]) * wsv[fn];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors, voff + 64 * fn, soff, 0);
             }
         }
     }
@@ -517,16 +556,21 @@ void gemm_tern4_kernel(LargeArgs args)
     const uint32_t w_off = (uint32_t)(tid >> 6) * (uint32_t)nblk * 1024u + 16u * wq;
     const int w_step = 4 * nblk * 1024;
     const uint32_t b_lds = (uint32_t)(wr * 64 + 16 * ((wq >> 4) ^ ((wr >> 2) & 3)));   // chunk swizzled by row
+    // Blocks past the last one (asked for by the pipeline near the end) are fetched from outside
+    // the buffer's range: they read as zeros without a trip to memory, so the final wait for
+    // them is short.
     auto load_w = [&](u4 (&dst)[2], int blk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < 2; s++) dst[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)w_off, 1024 * blk + s * w_step, 0);
+        for (int s = 0; s < 2; s++)
+            dst[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)w_off, blk < nblk ? 1024 * blk + s * w_step : (int)0x80000000u, 0);
     };
 
     // ---- activation codes: per slab the 512 token rows' AROW bytes go to Araw in AJ
     // instructions per wave-thread; instruction (s, wave) fills 1 KB of LDS, lane l the 16
     // bytes at chunk Q = 64 (4 s + wave) + l: row Q / (AROW / 16), chunk Q % (AROW / 16),
     // with the chunk index swizzled by row (INT4: by bit 3 of the row; INT8: by bits 2..3).
-    // Rows past M read as zero.  A pad digit's slab (k >= K) loads the last slab instead.
+    // Rows past M read as zero.  A pad digit's slab (k >= K) loads the last slab instead; slabs
+    // past the end of K are fetched from offset 2^31 and up (every buffer here is smaller).
     const auto ars = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(codes + (int64_t)m0 * crow), 0, (M - m0) * crow, 0x00020000);
     constexpr int CPR = AROW / 16;                      // 16-byte chunks per row and slab
@@ -541,7 +585,8 @@ void gemm_tern4_kernel(LargeArgs args)
     auto load_a = [&](int v, int slot) __attribute__((always_inline)) {
         int k = 320 * (v / 5) + 64 * (4 - v % 5);
         k = k < K ? k : K - 64;
-        const int kb = BITS == 8 ? k : k / 2;
+        // slabs past the last one: outside the buffer's range, as for the weights
+        const int kb = v < 5 * nblk ? (BITS == 8 ? k : k / 2) : (int)0x80000000u;
 #pragma unroll
         for (int s = 0; s < AJ; s++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(araw(slot) + 1024 * (4 * s + wave)), 16,
@@ -596,7 +641,7 @@ void gemm_tern4_kernel(LargeArgs args)
         for (int s = 0; s < 2; s++)
 #pragma unroll
             for (int w = 0; w < 4; w++) pb[s][w] = wnext[s][w];
-        load_w(wnext, next_blk < nblk ? next_blk : nblk - 1);
+        load_w(wnext, next_blk);
     };
 
     // Prologue: weights of block 0 (then 1 in flight); codes of slabs 0..3 in LDS; trits of
@@ -690,7 +735,11 @@ void gemm_tern4_kernel(LargeArgs args)
         // loads when one of them opened a block
         if (d >= 3) wait_vmcnt<2 * AJ + 2>();
         else wait_vmcnt<2 * AJ>();
-        block_sync();
+        // the trits of slab v + 2 written above must be visible to every wave before slab
+        // v + 1 reads them; after the second trit write come, behind scheduling barriers, the
+        // eight 16-byte B reads (ds_read_b128, which cannot be merged) and the A reads of four
+        // tiles (at least two instructions): at least 10 LDS reads, which may stay in flight
+        block_sync_reads_in_flight();
     };
     for (int blk = 0; blk < nblk; blk++) {
         const int v = 5 * blk;
@@ -723,6 +772,9 @@ void gemm_tern4_kernel(LargeArgs args)
                                   [&](int fn) __attribute__((always_inline)) {
                                       return group_scale(args.of, n0 / 16 + fn, w_scale);
                                   }, obase);
+    else if (DEQ && m0 + 128 * wave + 128 <= M && n0 + 128 <= N)
+        store_tiles_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N, sxf,
+                                    [&](int) __attribute__((always_inline)) { return w_scale; }, args.out);
     else
         store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
                                   [&](int) __attribute__((always_inline)) { return w_scale; }, obase);

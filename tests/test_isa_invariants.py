@@ -1,0 +1,51 @@
+"""Checks on the gfx950 assembly of the product kernels (compiled here with hipcc, no GPU).
+
+gemm_tern4_kernel ends every slab with `s_waitcnt lgkmcnt(10); s_barrier`: the barrier publishes
+the trits this wave wrote to LDS, and may leave the wave's last 10 LDS operations in flight.
+That is correct only if at least 10 LDS reads follow the last LDS write before each such
+barrier (LDS operations complete in order), which the source arranges with scheduling
+barriers; this test reads the compiled code of every instantiation to confirm it."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+CSRC = os.path.join(ROOT, "ternary_weight_bit_bitlinear_amd", "csrc")
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    return shutil.which("hipcc")
+
+
+@pytest.mark.skipif(hipcc() is None, reason="hipcc needed")
+def test_relaxed_barriers_follow_enough_lds_reads(tmp_path):
+    out = tmp_path / "gemm.s"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "gemm.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    kernels = re.split(r"\n(?=_ZN\S*gemm_tern4_kernel\S*:)", text)[1:]
+    assert len(kernels) >= 4
+    seen = 0
+    for k in kernels:
+        body = k.split(".Lfunc_end", 1)[0]
+        name = body.split(":", 1)[0]
+        reads, after_write = 0, False
+        for line in body.splitlines():
+            op = line.strip().split(" ", 1)[0]
+            if op.startswith("ds_write"):
+                reads, after_write = 0, True
+            elif op.startswith("ds_read"):
+                reads += 1
+            elif "lgkmcnt(10)" in line:
+                assert after_write and reads >= 10, f"{name}: {reads} reads after the last write"
+                seen += 1
+    assert seen >= 4 * 5
