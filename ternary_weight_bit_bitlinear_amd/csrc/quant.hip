@@ -207,6 +207,16 @@ __device__ __forceinline__ int quant_code(float x, float inv)
     return q;
 }
 
+// The code of x as the low bits of a float: fl(fl(x * inv) + 1.5 * 2^23) rounds fl(x * inv) to
+// the nearest integer, ties to even (the sum's unit in the last place is 1), and for
+// |fl(x * inv)| < 2^22 its low mantissa bits hold that integer in two's complement, so the low
+// byte (nibble) is the INT8 (INT4) code.  No clamp is needed: x is at most gamma in magnitude
+// and inv = fl(Qp / gamma), so |x * inv| <= Qp (1 + 2^-24), which rounds to at most Qp.
+__device__ __forceinline__ uint32_t code_bits(float x, float inv)
+{
+    return __builtin_bit_cast(uint32_t, x * inv + 12582912.0f);
+}
+
 // NORM: the row is first RMS-normalised, y[k] = (x[k] * r) * gain[k] with
 // r = fp32(1 / sqrt(sum_k x[k]^2 / K + eps)), the sum and r taken in double.
 template <int L, int BITS, bool HAD, bool NORM>
@@ -263,20 +273,21 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
             for (int j = 0; j < 4; j++) v[4 * r + j] = (v[4 * r + j] * rs) * gv[r][j];
     }
 
+    // For even L, c = 1/sqrt(K) = 2^(-L/2) exactly, and c * y is exact unless it falls below
+    // the normal range: then max |c y| = c max |y|, and fl(fl(c y) * inv) = fl(y * (c inv))
+    // with c inv exact, so the multiply by c folds into inv.  A row whose largest |y| is below
+    // 2^-100 (where c y might round) takes the multiply, as does a call that wants x_h.
+    constexpr bool FOLD = HAD && (L % 2 == 0);
     if constexpr (HAD) {
         butterflies<E, group_mask(L, G::LE, 0), 0, 2>(v);
         transform_groups<L, 1>(lds, t, v);
+        if constexpr (!FOLD) {
 #pragma unroll
-        for (int e = 0; e < E; e++) v[e] = v[e] * hadamard_c;
+            for (int e = 0; e < E; e++) v[e] = v[e] * hadamard_c;
+        }
     }
     constexpr uint32_t FM = final_mask<L, HAD>();
     const uint32_t tb = thread_bits<L, FM>(t);
-
-    if (xh != nullptr) {
-        float* xo = xh + m * K;
-#pragma unroll
-        for (int e = 0; e < E; e++) xo[tb | pdep((uint32_t)e, FM)] = v[e];
-    }
 
     // absmax over the row: exact, so the reduction order does not matter.
     float g = 0.0f;
@@ -290,7 +301,26 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
 #pragma unroll
     for (int w = 1; w < T / 64; w++) g = fmaxf(g, red[w]);
 
-    const float inv = g > 0.0f ? (float)QP / g : 0.0f;   // IEEE division
+    float vscale = 1.0f;   // the factor still to apply to v: c when it could not be folded
+    if constexpr (FOLD) {
+        if (xh != nullptr || g < 0x1p-100f) {
+#pragma unroll
+            for (int e = 0; e < E; e++) v[e] = v[e] * hadamard_c;
+            g = g * hadamard_c;
+        } else {
+            g = g * hadamard_c;   // exact: a power of two times a normal number
+            vscale = hadamard_c;
+        }
+    }
+
+    if (xh != nullptr) {
+        float* xo = xh + m * K;
+#pragma unroll
+        for (int e = 0; e < E; e++) xo[tb | pdep((uint32_t)e, FM)] = v[e];
+    }
+
+    const float inv0 = g > 0.0f ? (float)QP / g : 0.0f;   // IEEE division
+    const float inv = inv0 * vscale;                       // exact (power-of-two scaling)
     if (t == 0) scales[m] = g > 0.0f ? g / (float)QP : 0.0f;
 
     if constexpr (!HAD) {
@@ -303,9 +333,9 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
             uint32_t w = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int q = g > 0.0f ? quant_code<BITS>(v[4 * r + j], inv) : 0;
-                if constexpr (BITS == 8) w |= (uint32_t)(q & 255) << (8 * j);
-                else w |= (uint32_t)(q & 15) << (8 * j + 4 * (t & 1));
+                const uint32_t q = code_bits(v[4 * r + j], inv);
+                if constexpr (BITS == 8) w |= (q & 255u) << (8 * j);
+                else w |= (q & 15u) << (8 * j + 4 * (t & 1));
             }
             if constexpr (BITS == 8) {
                 *reinterpret_cast<uint32_t*>(codes + m * K + 4 * T * r + 4 * t) = w;
@@ -320,10 +350,7 @@ __global__ __launch_bounds__((Geometry<L, HAD>::T)) void quantize_rows_kernel(
     // Codes into LDS as bytes at position k, then out with 16-byte stores.
     int8_t* qb = reinterpret_cast<int8_t*>(lds);
 #pragma unroll
-    for (int e = 0; e < E; e++) {
-        int q = g > 0.0f ? quant_code<BITS>(v[e], inv) : 0;
-        qb[tb | pdep((uint32_t)e, FM)] = (int8_t)q;
-    }
+    for (int e = 0; e < E; e++) qb[tb | pdep((uint32_t)e, FM)] = (int8_t)code_bits(v[e], inv);
     __syncthreads();
     if constexpr (BITS == 8) {
         uint4* dst = reinterpret_cast<uint4*>(codes + m * K);
