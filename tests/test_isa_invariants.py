@@ -38,14 +38,19 @@ def test_relaxed_barriers_follow_enough_lds_reads(tmp_path):
     for k in kernels:
         body = k.split(".Lfunc_end", 1)[0]
         name = body.split(":", 1)[0]
-        reads, after_write = 0, False
+        reads, after_write, pending = 0, False, None
         for line in body.splitlines():
             op = line.strip().split(" ", 1)[0]
+            if pending is not None:
+                # the relaxed wait of a barrier: s_waitcnt lgkmcnt(10) right before s_barrier
+                if op == "s_barrier":
+                    assert pending[0] and pending[1] >= 10, f"{name}: {pending[1]} reads after the last write"
+                    seen += 1
+                pending = None
             if op.startswith("ds_write"):
                 reads, after_write = 0, True
             elif op.startswith("ds_read"):
                 reads += 1
-            elif "lgkmcnt(10)" in line:
-                assert after_write and reads >= 10, f"{name}: {reads} reads after the last write"
-                seen += 1
+            elif op == "s_waitcnt" and "lgkmcnt(10)" in line:
+                pending = (after_write, reads)
     assert seen >= 4 * 5
