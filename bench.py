@@ -772,6 +772,11 @@ def run_qkv_states(torch, tb, si, steps):
                                               state_codes=sc, state_scales=ss, stream=stream)
         for _ in range(2):
             once()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + 0.3      # settle the clocks
+        while time.perf_counter() < t_end:
+            once()
+            torch.cuda.synchronize()
         t = Timer(torch, steps)
         for _ in range(steps):
             t.begin(stream)

@@ -211,6 +211,35 @@ __device__ __forceinline__ void store_tiles_inside(const v4i (&acc)[FM][FN], int
     }
 }
 
+// store_tiles_glu for a wave tile wholly inside the M x F output (addressing as
+// store_tiles_inside, on the output columns col0 / 2 + 16 j + (l & 15)).
+template <int FM, int FN, int SHIFT, typename ScaleFn>
+__device__ __forceinline__ void store_tiles_glu_inside(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
+                                                       int F, ScaleFn sxf, float gate_scale, float up_scale,
+                                                       float* out)
+{
+    static_assert(FN % 2 == 0, "gate / up tiles come in pairs");
+    const int g = lane >> 4;
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc((void*)(out + (int64_t)row0 * F + col0 / 2), 0,
+                                                       0x7FFFFFFF, 0x00020000);
+    const int voff = 4 * (4 * g * F + (lane & 15));
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int soff = __builtin_amdgcn_readfirstlane(4 * (16 * fm + r) * F);
+#pragma unroll
+            for (int j = 0; j < FN / 2; j++) {
+                const float gv = ((float)(acc[fm][2 * j][r] >> SHIFT) * sx[r]) * gate_scale;
+                const float uv = ((float)(acc[fm][2 * j + 1][r] >> SHIFT) * sx[r]) * up_scale;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, silu_mul(gv, uv)), ors,
+                                                      voff + 64 * j, soff, 0);
+            }
+        }
+    }
+}
+
 // Gate / up pairs: tile columns 2j (gate rows) and 2j + 1 (the same up rows) of the grid above
 // give h = SiLU(gate) * up, each dequantised as in store_tiles with its own weight scale, in
 // column col0 / 2 + 16 j + (l & 15) of the M x F output (col0 a multiple of 32).
@@ -759,20 +788,27 @@ void gemm_tern4_kernel(LargeArgs args)
     auto sxf = [&](int fm) __attribute__((always_inline)) {
         return *(const f4*)&sxs[128 * wave + 16 * fm + 4 * g];
     };
-    if constexpr (EPI == kGlu)
-        store_tiles_glu<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, M, N / 2, sxf, args.of.gate_scale,
-                                 args.of.up_scale, obase);
-    else if constexpr (EPI == kStates)
+    // wave tiles wholly inside the output: no bounds tests (store_tiles_inside)
+    const bool inside = m0 + 128 * wave + 128 <= M && n0 + 128 <= N;
+    if constexpr (EPI == kGlu) {
+        if (inside)
+            store_tiles_glu_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N / 2, sxf, args.of.gate_scale,
+                                            args.of.up_scale, args.out);
+        else
+            store_tiles_glu<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, M, N / 2, sxf, args.of.gate_scale,
+                                     args.of.up_scale, obase);
+    } else if constexpr (EPI == kStates)
         store_tiles_states<8, 8, 4, SG>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
                                         [&](int fn) __attribute__((always_inline)) {
                                             return group_scale(args.of, n0 / 16 + fn, w_scale);
                                         }, args.of, (void*)args.out);
-    else if constexpr (EPI == kSegments)
-        store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
-                                  [&](int fn) __attribute__((always_inline)) {
-                                      return group_scale(args.of, n0 / 16 + fn, w_scale);
-                                  }, obase);
-    else if (DEQ && m0 + 128 * wave + 128 <= M && n0 + 128 <= N)
+    else if constexpr (EPI == kSegments) {
+        auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
+        if (DEQ && inside)
+            store_tiles_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N, sxf, wsf, args.out);
+        else
+            store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf, wsf, obase);
+    } else if (DEQ && inside)
         store_tiles_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N, sxf,
                                     [&](int) __attribute__((always_inline)) { return w_scale; }, args.out);
     else
