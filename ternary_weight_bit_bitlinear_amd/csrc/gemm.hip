@@ -41,6 +41,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BM = 256, BN = 256, NT = 512;       // INT8 kernel
 constexpr int BM4 = 512, BN4 = 128, NT4 = 256;    // INT4 kernel
+constexpr int NT4W = 512;                         // INT4 kernel, two waves per SIMD
 constexpr int LROW = 80;  // INT8 kernel: LDS bytes per tile row, 64 codes + 16 bytes of padding
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -103,13 +104,15 @@ __device__ __forceinline__ void block_sync()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The same barrier, but this wave's last 10 LDS operations may still be in flight.  LDS
+// The same barrier, but this wave's last N LDS operations may still be in flight.  LDS
 // operations complete in issue order, so every earlier one -- in particular every LDS write
 // the barrier publishes -- has completed.  For a caller whose last LDS write is followed by at
-// least 10 LDS reads it does not need before the barrier (the next slab's operands).
+// least N LDS reads it does not need before the barrier (the next slab's operands).
+template <int N = 10>
 __device__ __forceinline__ void block_sync_reads_in_flight()
 {
-    asm volatile("s_waitcnt lgkmcnt(10)\n\ts_barrier" ::: "memory");
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
 // v_mfma_i32_16x16x64_i8 with the accumulator tied to one set of accumulation registers
@@ -816,6 +819,241 @@ void gemm_tern4_kernel(LargeArgs args)
                                   [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
 }
 
+
+// gemm_tern4w_kernel: the INT4 product with two waves per SIMD.  Workgroup tile 512 tokens x
+// 128 outputs as in gemm_tern4_kernel, with the same five code slots and five trit slots in
+// LDS, but eight waves of 64 token rows x 128 outputs (4 x 8 MFMA tiles, 128 accumulation
+// registers), so that each wave fits in half of the SIMD's registers and the two waves of a
+// SIMD fill each other's gaps between MFMAs.  Per slab a wave issues 32 MFMAs; every thread
+// decodes one 16-byte piece of packed weights (four tern_steps) and widens its four A tiles.
+template <bool DEQ, int EPI, int SG = 0>
+__global__ __launch_bounds__(NT4W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_tern4w_kernel(LargeArgs args)
+{
+    constexpr int BM = BM4, BN = BN4, NT = NT4W;
+    constexpr int AROW = 32;                        // code bytes of one token row per slab
+    constexpr int AJ = BM * AROW / 16 / NT;         // 16-byte code loads per thread per slab
+    static_assert(AJ == 2, "two code loads per thread and slab");
+    __shared__ __align__(16) uint8_t A0[BM * AROW], A1[BM * AROW], A2[BM * AROW], A3[BM * AROW], A4[BM * AROW];
+    __shared__ __align__(16) uint8_t Bt[5][BN * 64];
+    __shared__ __align__(16) float sxs[BM];
+    auto araw = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+        return s == 0 ? A0 : s == 1 ? A1 : s == 2 ? A2 : s == 3 ? A3 : A4;
+    };
+
+    const int layer = blockIdx.z;
+    const int M = args.M, N = args.N, K = args.K;
+    const int crow = K / 2;
+    const uint8_t* codes = args.codes + (int64_t)layer * M * crow;
+    const uint8_t* packed = args.wptrs ? (const uint8_t*)((const_u64_ptr)(const void*)args.wptrs)[layer] : args.w0;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int nblk = (K + 319) / 320;
+    const int groups = (N + 15) / 16;
+
+    // ---- packed weights: thread tid holds piece tid & 63 of the tile (16 rows) tid >> 6.
+    const int g0 = n0 / 16;
+    const auto wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(packed + (int64_t)g0 * nblk * 1024), 0, (groups - g0) * nblk * 1024, 0x00020000);
+    const int wq = tid & 63, wr = 16 * (tid >> 6) + (wq & 15);
+    const uint32_t w_off = (uint32_t)(tid >> 6) * (uint32_t)nblk * 1024u + 16u * wq;
+    // chunk swizzled by bits 1..2 of the row: each eight consecutive lanes of a 16-byte LDS
+    // access (rows r..r+7 of one chunk column) then cover all 32 banks once
+    const uint32_t b_lds = (uint32_t)(wr * 64 + 16 * ((wq >> 4) ^ ((wr >> 1) & 3)));
+    auto load_w = [&](u4& dst, int blk) __attribute__((always_inline)) {
+        dst = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)w_off, blk < nblk ? 1024 * blk : (int)0x80000000u, 0);
+    };
+
+    // ---- activation codes: per slab the 512 rows' 32 bytes go to the code slot in two
+    // instructions per thread; instruction (s, wave) fills 1 KB, lane l the 16 bytes of chunk
+    // Q = 64 (8 s + wave) + l: row Q / 2, chunk Q % 2 swizzled by bit 3 of the row.
+    const auto ars = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(codes + (int64_t)m0 * crow), 0, (M - m0) * crow, 0x00020000);
+    uint32_t a_off;
+    {
+        const int Q = 64 * wave + lane, row = Q / 2, phys = Q % 2;
+        a_off = (uint32_t)row * (uint32_t)crow + 16u * (phys ^ ((row >> 3) & 1));
+    }
+    const int a_step = 256 * crow;                      // instruction s: 256 rows further
+    auto load_a = [&](int v, int slot) __attribute__((always_inline)) {
+        int k = 320 * (v / 5) + 64 * (4 - v % 5);
+        k = k < K ? k : K - 64;
+        const int kb = v < 5 * nblk ? k / 2 : (int)0x80000000u;
+#pragma unroll
+        for (int s = 0; s < AJ; s++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(araw(slot) + 1024 * (8 * s + wave)), 16,
+                                                     a_off, kb + s * a_step, 0, 0);
+    };
+
+    v4i acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int am = 64 * wave + (lane & 15), g = lane >> 4;
+    const uint32_t a_rd = (uint32_t)(am * 32 + 16 * ((g >> 1) ^ ((am >> 3) & 1)) + 8 * (g & 1));
+    const int brow = lane & 15;
+    const uint32_t b_rd = (uint32_t)(brow * 64 + 16 * (g ^ ((brow >> 1) & 3)));
+    typedef u2 ARaw;
+    auto read_a = [&](int slot, int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const ARaw*>(araw(slot) + a_rd + 16 * AROW * i);
+    };
+    auto read_b = [&](int slot, int n) __attribute__((always_inline)) {
+        return *reinterpret_cast<const v4i*>(Bt[slot] + b_rd + 1024 * n);
+    };
+    auto widen = [&](const ARaw& x) __attribute__((always_inline)) {
+        return v4i{(int)((x[0] << 4) & 0xF0F0F0F0u), (int)(x[0] & 0xF0F0F0F0u),
+                   (int)((x[1] << 4) & 0xF0F0F0F0u), (int)(x[1] & 0xF0F0F0F0u)};
+    };
+
+    u4 wnext;
+    uint32_t pb[4];
+    auto produce = [&](int p) __attribute__((always_inline)) {
+        u4 t;
+#pragma unroll
+        for (int w = 0; w < 4; w++) t[w] = tern_step(pb[w]);
+        *reinterpret_cast<u4*>(Bt[p] + b_lds) = t;
+    };
+    auto take_block = [&](int next_blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int w = 0; w < 4; w++) pb[w] = wnext[w];
+        load_w(wnext, next_blk);
+    };
+
+    // Prologue as in gemm_tern4_kernel.
+    load_w(wnext, 0);
+    load_a(0, 0);
+    load_a(1, 1);
+    load_a(2, 2);
+    load_a(3, 3);
+    constexpr int NSX = DEQ ? BM / NT : 0;
+    if constexpr (DEQ) {
+        const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)(args.scales + (int64_t)layer * M), 0, 4 * M, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr)(sxs + 64 * wave), 4,
+                                                 4u * (uint32_t)(m0 + 64 * wave + lane), 0, 0, 0);
+    }
+    wait_vmcnt<4 * AJ + NSX>();                         // the weight load of block 0
+    take_block(1);
+    produce(0);
+    produce(1);
+    wait_vmcnt<1>();                                    // all but block 1's weight load
+    block_sync();
+    v4i af[4], bf[8];
+    ARaw rn[4];                                         // packed A tiles of the next slab
+#pragma unroll
+    for (int i = 0; i < 3; i++) af[i] = widen(read_a(0, i));
+    rn[3] = read_a(0, 3);
+#pragma unroll
+    for (int n = 0; n < 8; n++) bf[n] = read_b(0, n);
+
+    // Slab v = 5 blk + d, slots as in gemm_tern4_kernel.  MFMAs row by row of A tiles: tile
+    // row 0 widens A tile 3 of v (read in the slab before), requests the codes of v + 4,
+    // reads the packed A tiles of v + 1 and decodes the next digit of the held weight words;
+    // rows 1, 2 and 3 widen A tiles 0, 1 and 2 of v + 1 (their registers are free once the
+    // row before is done); row 3 reads B tile n - 1 of v + 1 behind B tile n.  Every operand
+    // register is rewritten at least three MFMAs after the last MFMA that reads it.
+    auto mf = [&](int m, int n) __attribute__((always_inline)) { mfma_acc(acc[m][n], af[m], bf[n]); };
+    auto slab = [&](int v, int d) __attribute__((always_inline)) {
+        const int s1 = (d + 1) % 5, s2 = (d + 2) % 5, s4 = (d + 4) % 5;
+        u4 t;
+        mf(0, 0);
+        if (d == 3) take_block(v / 5 + 2);        // slab v + 2 opens block v / 5 + 1
+        load_a(v + 4, s4);
+        __builtin_amdgcn_sched_barrier(0);
+        mf(0, 1);
+        t[0] = tern_step(pb[0]);                  // at digit 0, pb < 3: q = 0
+        __builtin_amdgcn_sched_barrier(0);
+        mf(0, 2);
+        af[3] = widen(rn[3]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) rn[i] = read_a(s1, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 3; n < 8; n++) {
+            mf(0, n);
+            if (n == 3 || n == 5) t[n >> 1] = tern_step(pb[n >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mf(1, 0);
+        t[3] = tern_step(pb[3]);
+        *reinterpret_cast<u4*>(Bt[s2] + b_lds) = t;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 1; n < 8; n++) {
+            mf(1, n);
+            if (n == 2) af[0] = widen(rn[0]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            mf(2, n);
+            if (n == 2) af[1] = widen(rn[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            mf(3, n);
+            if (n >= 1) bf[n - 1] = read_b(s1, n - 1);
+            if (n == 4) af[2] = widen(rn[2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf[7] = read_b(s1, 7);
+        // codes of slab v + 2 in LDS before the barrier: issued since, AJ code loads in each of
+        // the last two slabs and one weight load when one of them opened a block
+        if (d >= 3) wait_vmcnt<2 * AJ + 1>();
+        else wait_vmcnt<2 * AJ>();
+        // after the trit write come, behind scheduling barriers, the eight B reads (ds_read_b128,
+        // which cannot be merged), which may stay in flight
+        block_sync_reads_in_flight<8>();
+    };
+    for (int blk = 0; blk < nblk; blk++) {
+        const int v = 5 * blk;
+        slab(v, 0);
+        slab(v + 1, 1);
+        slab(v + 2, 2);
+        slab(v + 3, 3);
+        slab(v + 4, 4);
+    }
+
+    wait_vmcnt<0>();
+    mfma_drain();
+
+    const float w_scale = args.wscales ? ((const_f32_ptr)(const void*)args.wscales)[layer] : args.wscale0;
+    void* obase = DEQ ? (void*)(args.out + (int64_t)layer * M * N) : (void*)(args.acc + (int64_t)layer * M * N);
+    auto sxf = [&](int fm) __attribute__((always_inline)) {
+        return *(const f4*)&sxs[64 * wave + 16 * fm + 4 * g];
+    };
+    const int row0 = m0 + 64 * wave;
+    const bool inside = row0 + 64 <= M && n0 + 128 <= N;
+    if constexpr (EPI == kGlu) {
+        if (inside)
+            store_tiles_glu_inside<4, 8, 4>(acc, row0, n0, lane, N / 2, sxf, args.of.gate_scale,
+                                            args.of.up_scale, args.out);
+        else
+            store_tiles_glu<4, 8, 4>(acc, row0, n0, lane, M, N / 2, sxf, args.of.gate_scale,
+                                     args.of.up_scale, obase);
+    } else if constexpr (EPI == kStates)
+        store_tiles_states<4, 8, 4, SG>(acc, row0, n0, lane, M, N, sxf,
+                                        [&](int fn) __attribute__((always_inline)) {
+                                            return group_scale(args.of, n0 / 16 + fn, w_scale);
+                                        }, args.of, (void*)args.out);
+    else if constexpr (EPI == kSegments) {
+        auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
+        if (DEQ && inside)
+            store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf, wsf, args.out);
+        else
+            store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf, wsf, obase);
+    } else if (DEQ && inside)
+        store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf,
+                                    [&](int) __attribute__((always_inline)) { return w_scale; }, args.out);
+    else
+        store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf,
+                                  [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
@@ -837,12 +1075,12 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
         return hipErrorInvalidValue;
     if (bits == 4) {
         dim3 grid((N + BN4 - 1) / BN4, (M + BM4 - 1) / BM4, L);
-        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 8>), grid, dim3(NT4), 0, stream, a);
-        else if (of.states) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 4>), grid, dim3(NT4), 0, stream, a);
-        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);
-        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4_kernel<true, kSegments>), grid, dim3(NT4), 0, stream, a);
-        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4_kernel<true, kPlain>), grid, dim3(NT4), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_tern4_kernel<false, kPlain>), grid, dim3(NT4), 0, stream, a);
+        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kStates, 8>), grid, dim3(NT4W), 0, stream, a);
+        else if (of.states) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kStates, 4>), grid, dim3(NT4W), 0, stream, a);
+        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kGlu>), grid, dim3(NT4W), 0, stream, a);
+        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kSegments>), grid, dim3(NT4W), 0, stream, a);
+        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kPlain>), grid, dim3(NT4W), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern4w_kernel<false, kPlain>), grid, dim3(NT4W), 0, stream, a);
     } else {
         dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, L);
         if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kGlu>), grid, dim3(NT), 0, stream, a);

@@ -1,10 +1,10 @@
 """Checks on the gfx950 assembly of the product kernels (compiled here with hipcc, no GPU).
 
-gemm_tern4_kernel ends every slab with `s_waitcnt lgkmcnt(10); s_barrier`: the barrier publishes
-the trits this wave wrote to LDS, and may leave the wave's last 10 LDS operations in flight.
-That is correct only if at least 10 LDS reads follow the last LDS write before each such
-barrier (LDS operations complete in order), which the source arranges with scheduling
-barriers; this test reads the compiled code of every instantiation to confirm it."""
+The INT4 product kernels end every slab with `s_waitcnt lgkmcnt(N); s_barrier` (N > 0): the
+barrier publishes the trits this wave wrote to LDS, and may leave the wave's last N LDS
+operations in flight.  That is correct only if at least N LDS reads follow the last LDS write
+before each such barrier (LDS operations complete in order), which the source arranges with
+scheduling barriers; this test reads the compiled code of every instantiation to confirm it."""
 import os
 import re
 import shutil
@@ -32,7 +32,7 @@ def test_relaxed_barriers_follow_enough_lds_reads(tmp_path):
            "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "gemm.hip")]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     text = out.read_text()
-    kernels = re.split(r"\n(?=_ZN\S*gemm_tern4_kernel\S*:)", text)[1:]
+    kernels = re.split(r"\n(?=_ZN\S*gemm_tern4\w*_kernel\S*:)", text)[1:]
     assert len(kernels) >= 4
     seen = 0
     for k in kernels:
@@ -42,15 +42,18 @@ def test_relaxed_barriers_follow_enough_lds_reads(tmp_path):
         for line in body.splitlines():
             op = line.strip().split(" ", 1)[0]
             if pending is not None:
-                # the relaxed wait of a barrier: s_waitcnt lgkmcnt(10) right before s_barrier
+                # the relaxed wait of a barrier: s_waitcnt lgkmcnt(N) right before s_barrier
                 if op == "s_barrier":
-                    assert pending[0] and pending[1] >= 10, f"{name}: {pending[1]} reads after the last write"
+                    after, nreads, n = pending
+                    assert after and nreads >= n, f"{name}: {nreads} reads after the last write, lgkmcnt({n})"
                     seen += 1
                 pending = None
             if op.startswith("ds_write"):
                 reads, after_write = 0, True
             elif op.startswith("ds_read"):
                 reads += 1
-            elif op == "s_waitcnt" and "lgkmcnt(10)" in line:
-                pending = (after_write, reads)
+            elif op == "s_waitcnt":
+                m = re.search(r"lgkmcnt\((\d+)\)", line)
+                if m and int(m.group(1)) > 0:
+                    pending = (after_write, reads, int(m.group(1)))
     assert seen >= 4 * 5
