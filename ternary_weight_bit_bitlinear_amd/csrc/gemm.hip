@@ -29,6 +29,8 @@
 //   gemm_tern_kernel (INT8 activations).  Workgroup tile 256 x 256, eight waves (two per SIMD)
 //     of 128 x 64; per slab the MFMAs read one pair of LDS buffers while the next slab's trits
 //     and codes are written to the other pair; global loads run ahead in registers.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bitnet {
@@ -941,63 +943,40 @@ void gemm_tern4w_kernel(LargeArgs args)
     produce(1);
     wait_vmcnt<1>();                                    // all but block 1's weight load
     block_sync();
-    v4i af[4], bf[8];
+    v4i af[2][4], bf[8];                                // A operands of slabs of even / odd index
     ARaw rn[4];                                         // packed A tiles of the next slab
 #pragma unroll
-    for (int i = 0; i < 3; i++) af[i] = widen(read_a(0, i));
-    rn[3] = read_a(0, 3);
+    for (int i = 0; i < 4; i++) af[0][i] = widen(read_a(0, i));
 #pragma unroll
     for (int n = 0; n < 8; n++) bf[n] = read_b(0, n);
 
-    // Slab v = 5 blk + d, slots as in gemm_tern4_kernel.  MFMAs row by row of A tiles: tile
-    // row 0 widens A tile 3 of v (read in the slab before), requests the codes of v + 4,
-    // reads the packed A tiles of v + 1 and decodes the next digit of the held weight words;
-    // rows 1, 2 and 3 widen A tiles 0, 1 and 2 of v + 1 (their registers are free once the
-    // row before is done); row 3 reads B tile n - 1 of v + 1 behind B tile n.  Every operand
-    // register is rewritten at least three MFMAs after the last MFMA that reads it.
-    auto mf = [&](int m, int n) __attribute__((always_inline)) { mfma_acc(acc[m][n], af[m], bf[n]); };
-    auto slab = [&](int v, int d) __attribute__((always_inline)) {
+    // Slab v = 5 blk + d, slots as in gemm_tern4_kernel.  The 32 MFMAs go B tile by B tile
+    // (MFMA slot 4 n + m is A tile m x B tile n), so B tile n is free once slot 4 n + 3 is
+    // issued: its operand of v + 1 is read behind slot 4 n + 5 and has the rest of the slab to
+    // arrive.  The A operands of v + 1 go to the other register set (v odd / even), widened
+    // from packed tiles read at slot 1.  Slot 0 requests the codes of v + 4; slots 2, 6, 10 and
+    // 14 decode the next digit of the held weight words, written as the trits of v + 2 after
+    // slot 14; slots 18, 22, 26 and 30 widen the A tiles of v + 1.
+    auto slab = [&](int v, int d, auto parity, bool last = false) __attribute__((always_inline)) {
+        constexpr int P = decltype(parity)::value, Q = 1 - P;
         const int s1 = (d + 1) % 5, s2 = (d + 2) % 5, s4 = (d + 4) % 5;
         u4 t;
-        mf(0, 0);
-        if (d == 3) take_block(v / 5 + 2);        // slab v + 2 opens block v / 5 + 1
-        load_a(v + 4, s4);
-        __builtin_amdgcn_sched_barrier(0);
-        mf(0, 1);
-        t[0] = tern_step(pb[0]);                  // at digit 0, pb < 3: q = 0
-        __builtin_amdgcn_sched_barrier(0);
-        mf(0, 2);
-        af[3] = widen(rn[3]);
 #pragma unroll
-        for (int i = 0; i < 4; i++) rn[i] = read_a(s1, i);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 32; j++) {
+            const int n = j >> 2, m = j & 3;
+            mfma_acc(acc[m][n], af[P][m], bf[n]);
+            if (j == 0) {
+                if (d == 3) take_block(v / 5 + 2);    // slab v + 2 opens block v / 5 + 1
+                load_a(v + 4, s4);
+            }
+            if (j == 1) {
 #pragma unroll
-        for (int n = 3; n < 8; n++) {
-            mf(0, n);
-            if (n == 3 || n == 5) t[n >> 1] = tern_step(pb[n >> 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mf(1, 0);
-        t[3] = tern_step(pb[3]);
-        *reinterpret_cast<u4*>(Bt[s2] + b_lds) = t;
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = 1; n < 8; n++) {
-            mf(1, n);
-            if (n == 2) af[0] = widen(rn[0]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-            mf(2, n);
-            if (n == 2) af[1] = widen(rn[1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-            mf(3, n);
-            if (n >= 1) bf[n - 1] = read_b(s1, n - 1);
-            if (n == 4) af[2] = widen(rn[2]);
+                for (int i = 0; i < 4; i++) rn[i] = read_a(s1, i);
+            }
+            if (j == 2 || j == 6 || j == 10 || j == 14) t[j >> 2] = tern_step(pb[j >> 2]);   // at digit 0, pb < 3: q = 0
+            if (j == 14) *reinterpret_cast<u4*>(Bt[s2] + b_lds) = t;
+            if ((j & 3) == 1 && j >= 5) bf[(j >> 2) - 1] = read_b(s1, (j >> 2) - 1);
+            if (j == 18 || j == 22 || j == 26 || j == 30) af[Q][(j - 18) >> 2] = widen(rn[(j - 18) >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
         bf[7] = read_b(s1, 7);
@@ -1005,17 +984,37 @@ void gemm_tern4w_kernel(LargeArgs args)
         // the last two slabs and one weight load when one of them opened a block
         if (d >= 3) wait_vmcnt<2 * AJ + 1>();
         else wait_vmcnt<2 * AJ>();
-        // after the trit write come, behind scheduling barriers, the eight B reads (ds_read_b128,
-        // which cannot be merged), which may stay in flight
-        block_sync_reads_in_flight<8>();
+        // after the trit write come, behind scheduling barriers, the B reads of tiles 3..7
+        // (ds_read_b128, which cannot be merged), which may stay in flight -- except in the
+        // last slab of the tile, whose reads of a next slab are dropped as unused
+        if (last) block_sync();
+        else block_sync_reads_in_flight<5>();
     };
-    for (int blk = 0; blk < nblk; blk++) {
+    // Two blocks per iteration, so that the register set of each slab is known at compile
+    // time (slab v uses set v & 1); an odd last block starts on an even slab.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int blk = 0;
+    for (; blk + 1 < nblk; blk += 2) {
         const int v = 5 * blk;
-        slab(v, 0);
-        slab(v + 1, 1);
-        slab(v + 2, 2);
-        slab(v + 3, 3);
-        slab(v + 4, 4);
+        slab(v, 0, P0{});
+        slab(v + 1, 1, P1{});
+        slab(v + 2, 2, P0{});
+        slab(v + 3, 3, P1{});
+        slab(v + 4, 4, P0{});
+        slab(v + 5, 0, P1{});
+        slab(v + 6, 1, P0{});
+        slab(v + 7, 2, P1{});
+        slab(v + 8, 3, P0{});
+        slab(v + 9, 4, P1{});
+    }
+    if (blk < nblk) {
+        const int v = 5 * blk;
+        slab(v, 0, P0{});
+        slab(v + 1, 1, P1{});
+        slab(v + 2, 2, P0{});
+        slab(v + 3, 3, P1{});
+        slab(v + 4, 4, P0{}, true);
     }
 
     wait_vmcnt<0>();
