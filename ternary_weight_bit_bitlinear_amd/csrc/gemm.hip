@@ -879,14 +879,17 @@ void gemm_tern4w_kernel(LargeArgs args)
         a_off = (uint32_t)row * (uint32_t)crow + 16u * (phys ^ ((row >> 3) & 1));
     }
     const int a_step = 256 * crow;                      // instruction s: 256 rows further
-    auto load_a = [&](int v, int slot) __attribute__((always_inline)) {
+    // instruction s of the code request of slab v (rows 256 s .. 256 s + 255 of the tile)
+    auto load_a_part = [&](int v, int slot, int s) __attribute__((always_inline)) {
         int k = 320 * (v / 5) + 64 * (4 - v % 5);
         k = k < K ? k : K - 64;
         const int kb = v < 5 * nblk ? k / 2 : (int)0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(araw(slot) + 1024 * (8 * s + wave)), 16,
+                                                 a_off, kb + s * a_step, 0, 0);
+    };
+    auto load_a = [&](int v, int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < AJ; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(araw(slot) + 1024 * (8 * s + wave)), 16,
-                                                     a_off, kb + s * a_step, 0, 0);
+        for (int s = 0; s < AJ; s++) load_a_part(v, slot, s);
     };
 
     v4i acc[4][8];
@@ -965,10 +968,12 @@ void gemm_tern4w_kernel(LargeArgs args)
         for (int j = 0; j < 32; j++) {
             const int n = j >> 2, m = j & 3;
             mfma_acc(acc[m][n], af[P][m], bf[n]);
+            // the code request of v + 4, its two instructions half a slab apart
             if (j == 0) {
                 if (d == 3) take_block(v / 5 + 2);    // slab v + 2 opens block v / 5 + 1
-                load_a(v + 4, s4);
+                load_a_part(v + 4, s4, 0);
             }
+            if (j == 16) load_a_part(v + 4, s4, 1);
             if (j == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) rn[i] = read_a(s1, i);
