@@ -14,14 +14,14 @@
 //
 // Two kernels:
 //   gemm_tern4_kernel (INT4 activations, the BitNet v2 case).  Workgroup tile 512 tokens x
-//     128 outputs, four waves (one per SIMD), each 128 x 128 outputs (8 x 8 MFMA tiles, int32
+//     128 outputs, eight waves (two per SIMD), each 64 x 128 outputs (4 x 8 MFMA tiles, int32
 //     accumulators in the accumulation registers).  The tile is tall because the unpacked
 //     trits of a weight row serve every token row of the tile.  Per slab the codes go from
 //     global memory straight into LDS (buffer loads with the LDS as destination), four slabs
 //     ahead and still packed; every thread turns the next digit of the packed words it holds
-//     into trits for two slabs ahead; each wave issues the 64 MFMAs of the slab from
+//     into trits for two slabs ahead; each wave issues the 32 MFMAs of the slab from
 //     registers and, in their shadow, reads its operands of the next slab -- weight trits and
-//     its own 128 rows of codes, widened in registers.  A short last block keeps its pad
+//     its own 64 rows of codes, widened in registers.  A short last block keeps its pad
 //     digits (trits 0), so every block has five slabs and slot d of the five LDS slots holds
 //     digit 4 - d.  Widening needs no sign arithmetic: a nibble moved to the high half of a
 //     byte is the int8 value 16 x code, so the MFMA sums are 16 x the code sums and one
@@ -42,8 +42,7 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BM = 256, BN = 256, NT = 512;       // INT8 kernel
-constexpr int BM4 = 512, BN4 = 128, NT4 = 256;    // INT4 kernel
-constexpr int NT4W = 512;                         // INT4 kernel, two waves per SIMD
+constexpr int BM4 = 512, BN4 = 128, NT4 = 512;    // INT4 kernel
 constexpr int LROW = 80;  // INT8 kernel: LDS bytes per tile row, 64 codes + 16 bytes of padding
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -549,290 +548,15 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
 }
 
 
+// gemm_tern4_kernel: see the head of the file.  Each wave holds 4 x 8 MFMA tiles (128
+// accumulation registers) and fits in half of its SIMD's registers, so the two waves of a SIMD
+// fill each other's gaps between MFMAs.  Per slab a wave issues 32 MFMAs; every thread decodes
+// one 16-byte piece of packed weights (four tern_steps) and widens its own four A tiles.
 template <bool DEQ, int EPI, int SG = 0>
-__global__ __launch_bounds__(NT4) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NT4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tern4_kernel(LargeArgs args)
 {
-    constexpr int BITS = 4, BM = BM4, BN = BN4, NT = NT4;
-    constexpr int AROW = 32;                        // code bytes of one token row per slab
-    constexpr int AJ = BM * AROW / 16 / NT;         // 16-byte code loads per thread per slab
-    // Five slots of codes and of trits, one per digit of a block, each slot its own array so
-    // that the compiler sees the loads into one slot do not touch the others.
-    __shared__ __align__(16) uint8_t A0[BM * AROW], A1[BM * AROW], A2[BM * AROW], A3[BM * AROW], A4[BM * AROW];
-    __shared__ __align__(16) uint8_t Bt[5][BN * 64];
-    __shared__ __align__(16) float sxs[BM];         // s_x of the tile's rows, for the epilogue
-    auto araw = [&](int s) __attribute__((always_inline)) -> uint8_t* {
-        return s == 0 ? A0 : s == 1 ? A1 : s == 2 ? A2 : s == 3 ? A3 : A4;
-    };
-
-    // Layer blockIdx.z of a grouped call.
-    const int layer = blockIdx.z;
-    const int M = args.M, N = args.N, K = args.K;
-    const int crow = BITS == 8 ? K : K / 2;             // code bytes per activation row
-    const uint8_t* codes = args.codes + (int64_t)layer * M * crow;
-    const uint8_t* packed = args.wptrs ? (const uint8_t*)((const_u64_ptr)(const void*)args.wptrs)[layer] : args.w0;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int nblk = (K + 319) / 320;
-    const int groups = (N + 15) / 16;
-
-    // ---- packed weights: a block of 16 rows x 64 bytes is one contiguous 1 KB tile whose
-    // 16-byte piece q = 16 c + r holds bytes 16c..16c+15 of row r.  Thread tid holds pieces
-    // p = tid + 256 s (s = 0, 1): piece p & 63 of tile p >> 6.  Buffer loads: tiles past the
-    // last row group read as zero (their outputs are never stored).
-    const int g0 = n0 / 16;
-    const auto wrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(packed + (int64_t)g0 * nblk * 1024), 0, (groups - g0) * nblk * 1024, 0x00020000);
-    // piece tid: tile tid >> 6, q = tid & 63; piece tid + 256: four tiles (64 rows) further
-    const int wq = tid & 63, wr = 16 * (tid >> 6) + (wq & 15);
-    const uint32_t w_off = (uint32_t)(tid >> 6) * (uint32_t)nblk * 1024u + 16u * wq;
-    const int w_step = 4 * nblk * 1024;
-    const uint32_t b_lds = (uint32_t)(wr * 64 + 16 * ((wq >> 4) ^ ((wr >> 2) & 3)));   // chunk swizzled by row
-    // Blocks past the last one (asked for by the pipeline near the end) are fetched from outside
-    // the buffer's range: they read as zeros without a trip to memory, so the final wait for
-    // them is short.
-    auto load_w = [&](u4 (&dst)[2], int blk) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-            dst[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)w_off, blk < nblk ? 1024 * blk + s * w_step : (int)0x80000000u, 0);
-    };
-
-    // ---- activation codes: per slab the 512 token rows' AROW bytes go to Araw in AJ
-    // instructions per wave-thread; instruction (s, wave) fills 1 KB of LDS, lane l the 16
-    // bytes at chunk Q = 64 (4 s + wave) + l: row Q / (AROW / 16), chunk Q % (AROW / 16),
-    // with the chunk index swizzled by row (INT4: by bit 3 of the row; INT8: by bits 2..3).
-    // Rows past M read as zero.  A pad digit's slab (k >= K) loads the last slab instead; slabs
-    // past the end of K are fetched from offset 2^31 and up (every buffer here is smaller).
-    const auto ars = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(codes + (int64_t)m0 * crow), 0, (M - m0) * crow, 0x00020000);
-    constexpr int CPR = AROW / 16;                      // 16-byte chunks per row and slab
-    // Instruction s covers rows 256 s / CPR further than instruction 0 with the same swizzle.
-    uint32_t a_off;
-    {
-        const int Q = 64 * wave + lane, row = Q / CPR, phys = Q % CPR;
-        const int c = BITS == 8 ? phys ^ ((row >> 2) & 3) : phys ^ ((row >> 3) & 1);
-        a_off = (uint32_t)row * (uint32_t)crow + 16u * c;
-    }
-    const int a_step = 256 / CPR * crow;
-    auto load_a = [&](int v, int slot) __attribute__((always_inline)) {
-        int k = 320 * (v / 5) + 64 * (4 - v % 5);
-        k = k < K ? k : K - 64;
-        // slabs past the last one: outside the buffer's range, as for the weights
-        const int kb = v < 5 * nblk ? (BITS == 8 ? k : k / 2) : (int)0x80000000u;
-#pragma unroll
-        for (int s = 0; s < AJ; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_ptr)(araw(slot) + 1024 * (4 * s + wave)), 16,
-                                                     a_off, kb + s * a_step, 0, 0);
-    };
-
-    v4i acc[8][8];   // this wave's 128 x 128 outputs
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) acc[i][j] = v4i{0, 0, 0, 0};
-
-    // ---- operands.  MFMA lane l: A row (l & 15) of the 16-row tile, B row (l & 15), k-slots
-    // 16 g .. 16 g + 15 with g = l >> 4.
-    const int am = 128 * wave + (lane & 15), g = lane >> 4;
-    // Fragment i of a 16-row tile sits 16 rows below fragment 0, with the same swizzle.
-    uint32_t a_rd, b_rd;
-    {
-        const int row = am;
-        if constexpr (BITS == 8)
-            a_rd = (uint32_t)(row * 64 + 16 * (g ^ ((row >> 2) & 3)));
-        else
-            a_rd = (uint32_t)(row * 32 + 16 * ((g >> 1) ^ ((row >> 3) & 1)) + 8 * (g & 1));
-        const int brow = lane & 15;
-        b_rd = (uint32_t)(brow * 64 + 16 * (g ^ ((brow >> 2) & 3)));
-    }
-    typedef u2 ARaw;
-    auto read_a = [&](int slot, int i) __attribute__((always_inline)) {
-        return *reinterpret_cast<const ARaw*>(araw(slot) + a_rd + 16 * AROW * i);
-    };
-    // INT4: 16 codes (two words, code 8w + p in the low nibble of byte p, 8w + p + 4 in the
-    // high nibble) -> 16 bytes of 16 x code
-    auto widen = [&](const ARaw& x) __attribute__((always_inline)) {
-        return v4i{(int)((x[0] << 4) & 0xF0F0F0F0u), (int)(x[0] & 0xF0F0F0F0u),
-                   (int)((x[1] << 4) & 0xF0F0F0F0u), (int)(x[1] & 0xF0F0F0F0u)};
-    };
-
-    // ---- weight decoding of one slab into Bt slot p: the next digit of the held words.
-    u4 wnext[2];
-    uint32_t pb[2][4];
-    auto produce = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-            u4 t;
-#pragma unroll
-            for (int w = 0; w < 4; w++) t[w] = tern_step(pb[s][w]);   // at digit 0, pb < 3: q = 0
-            *reinterpret_cast<u4*>(Bt[p] + b_lds + 4096 * s) = t;
-        }
-    };
-    auto take_block = [&](int next_blk) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-#pragma unroll
-            for (int w = 0; w < 4; w++) pb[s][w] = wnext[s][w];
-        load_w(wnext, next_blk);
-    };
-
-    // Prologue: weights of block 0 (then 1 in flight); codes of slabs 0..3 in LDS; trits of
-    // slabs 0 and 1; operands of slab 0 in registers (A tiles 4..7 still packed).  The codes
-    // and scales are requested together with the first weights, so the prologue waits for
-    // one round trip to memory, not two.
-    load_w(wnext, 0);
-    load_a(0, 0);
-    load_a(1, 1);
-    load_a(2, 2);
-    load_a(3, 3);
-    constexpr int NSX = DEQ ? BM / NT : 0;            // scale loads
-    if constexpr (DEQ) {
-        // s_x of the tile's rows straight into LDS, 64 rows per wave-wide load; rows past M
-        // read as zero.
-        const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)(args.scales + (int64_t)layer * M), 0, 4 * M, 0x00020000);
-#pragma unroll
-        for (int s = 0; s < NSX; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr)(sxs + NT * s + 64 * wave), 4,
-                                                     4u * (uint32_t)(m0 + NT * s + 64 * wave + lane), 0, 0, 0);
-    }
-    wait_vmcnt<4 * AJ + NSX>();                         // the two weight loads of block 0
-    take_block(1);
-    produce(0);
-    produce(1);
-    wait_vmcnt<2>();                                    // all but block 1's two weight loads
-    block_sync();
-    v4i af[8], bf[8];
-    ARaw rhi[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        af[i] = widen(read_a(0, i));
-        rhi[i] = read_a(0, 4 + i);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) bf[i] = *reinterpret_cast<const v4i*>(Bt[0] + b_rd + 1024 * i);
-
-    // Slab v = 5 blk + d (digit 4 - d of block blk), slots indexed by d: MFMAs of v; operand
-    // reads of v + 1 (slots d + 1); trits of v + 2 into Bt slot d + 2; codes of v + 4 into
-    // code slot d + 4 (all mod 5).  With one wave per SIMD, the vector work only overlaps the
-    // matrix core if it sits between the MFMAs, so the slab is written as a fixed sequence of
-    // short chunks -- a few MFMAs and a little vector or LDS work each -- separated by
-    // scheduling barriers that keep the compiler from regrouping them.
-    //   first half (A tiles 0..3 x B tiles 0..7): packed A tiles 0..3 of v + 1 requested, the
-    //     next digit of the held weight words decoded and written, A tiles 4..7 of v widened;
-    //   second half (A tiles 4..7 x B tiles 0..7): B tile n - 1 of v + 1 read behind B tile
-    //     n's MFMAs, A tiles 0..3 of v + 1 widened, packed A tiles 4..7 of v + 1 requested.
-    auto mf = [&](int m, int n) __attribute__((always_inline)) { mfma_acc(acc[m][n], af[m], bf[n]); };
-    auto slab = [&](int v, int d) __attribute__((always_inline)) {
-        const int s1 = (d + 1) % 5, s2 = (d + 2) % 5, s4 = (d + 4) % 5;
-        ARaw rlo[4];
-        u4 t[2];
-        mf(0, 0);
-        mf(1, 0);
-        if (d == 3) take_block(v / 5 + 2);        // slab v + 2 opens block v / 5 + 1
-        load_a(v + 4, s4);
-#pragma unroll
-        for (int i = 0; i < 4; i++) rlo[i] = read_a(s1, i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int c = k + 1;
-            mf(2 * (c & 1), c >> 1);
-            mf(2 * (c & 1) + 1, c >> 1);
-            t[k >> 2][k & 3] = tern_step(pb[k >> 2][k & 3]);   // at digit 0, pb < 3: q = 0
-            if ((k & 3) == 3) *reinterpret_cast<u4*>(Bt[s2] + b_lds + 4096 * (k >> 2)) = t[k >> 2];
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int c = 9; c < 16; c++) {
-            mf(2 * (c & 1), c >> 1);
-            mf(2 * (c & 1) + 1, c >> 1);
-            if (c < 13) af[4 + c - 9] = widen(rhi[c - 9]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-            mf(4, n);
-            mf(5, n);
-            mf(6, n);
-            mf(7, n);
-            if (n >= 1) bf[n - 1] = *reinterpret_cast<const v4i*>(Bt[s1] + b_rd + 1024 * (n - 1));
-            if (n >= 2 && n < 6) af[n - 2] = widen(rlo[n - 2]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        bf[7] = *reinterpret_cast<const v4i*>(Bt[s1] + b_rd + 1024 * 7);
-#pragma unroll
-        for (int i = 0; i < 4; i++) rhi[i] = read_a(s1, 4 + i);
-        // the codes of slab v + 2 (issued two slabs earlier) must be in LDS before the
-        // barrier; issued since: AJ code loads in each of the last two slabs, and two weight
-        // loads when one of them opened a block
-        if (d >= 3) wait_vmcnt<2 * AJ + 2>();
-        else wait_vmcnt<2 * AJ>();
-        // the trits of slab v + 2 written above must be visible to every wave before slab
-        // v + 1 reads them; after the second trit write come, behind scheduling barriers, the
-        // eight 16-byte B reads (ds_read_b128, which cannot be merged) and the A reads of four
-        // tiles (at least two instructions): at least 10 LDS reads, which may stay in flight
-        block_sync_reads_in_flight();
-    };
-    for (int blk = 0; blk < nblk; blk++) {
-        const int v = 5 * blk;
-        slab(v, 0);
-        slab(v + 1, 1);
-        slab(v + 2, 2);
-        slab(v + 3, 3);
-        slab(v + 4, 4);
-    }
-
-    wait_vmcnt<0>();   // the loads issued past the last slab
-    mfma_drain();
-
-    // The codes entered the MFMAs as 16 x code, so the sums are 16 x the integer dot products.
-    const float w_scale = args.wscales ? ((const_f32_ptr)(const void*)args.wscales)[layer] : args.wscale0;
-    void* obase = DEQ ? (void*)(args.out + (int64_t)layer * M * N) : (void*)(args.acc + (int64_t)layer * M * N);
-    auto sxf = [&](int fm) __attribute__((always_inline)) {
-        return *(const f4*)&sxs[128 * wave + 16 * fm + 4 * g];
-    };
-    // wave tiles wholly inside the output: no bounds tests (store_tiles_inside)
-    const bool inside = m0 + 128 * wave + 128 <= M && n0 + 128 <= N;
-    if constexpr (EPI == kGlu) {
-        if (inside)
-            store_tiles_glu_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N / 2, sxf, args.of.gate_scale,
-                                            args.of.up_scale, args.out);
-        else
-            store_tiles_glu<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, M, N / 2, sxf, args.of.gate_scale,
-                                     args.of.up_scale, obase);
-    } else if constexpr (EPI == kStates)
-        store_tiles_states<8, 8, 4, SG>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
-                                        [&](int fn) __attribute__((always_inline)) {
-                                            return group_scale(args.of, n0 / 16 + fn, w_scale);
-                                        }, args.of, (void*)args.out);
-    else if constexpr (EPI == kSegments) {
-        auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
-        if (DEQ && inside)
-            store_tiles_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N, sxf, wsf, args.out);
-        else
-            store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf, wsf, obase);
-    } else if (DEQ && inside)
-        store_tiles_inside<8, 8, 4>(acc, m0 + 128 * wave, n0, lane, N, sxf,
-                                    [&](int) __attribute__((always_inline)) { return w_scale; }, args.out);
-    else
-        store_tiles<8, 8, 4, DEQ>(acc, m0 + 128 * wave, n0, lane, M, N, sxf,
-                                  [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
-}
-
-
-// gemm_tern4w_kernel: the INT4 product with two waves per SIMD.  Workgroup tile 512 tokens x
-// 128 outputs as in gemm_tern4_kernel, with the same five code slots and five trit slots in
-// LDS, but eight waves of 64 token rows x 128 outputs (4 x 8 MFMA tiles, 128 accumulation
-// registers), so that each wave fits in half of the SIMD's registers and the two waves of a
-// SIMD fill each other's gaps between MFMAs.  Per slab a wave issues 32 MFMAs; every thread
-// decodes one 16-byte piece of packed weights (four tern_steps) and widens its four A tiles.
-template <bool DEQ, int EPI, int SG = 0>
-__global__ __launch_bounds__(NT4W) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_tern4w_kernel(LargeArgs args)
-{
-    constexpr int BM = BM4, BN = BN4, NT = NT4W;
+    constexpr int BM = BM4, BN = BN4, NT = NT4;
     constexpr int AROW = 32;                        // code bytes of one token row per slab
     constexpr int AJ = BM * AROW / 16 / NT;         // 16-byte code loads per thread per slab
     static_assert(AJ == 2, "two code loads per thread and slab");
@@ -928,7 +652,9 @@ void gemm_tern4w_kernel(LargeArgs args)
         load_w(wnext, next_blk);
     };
 
-    // Prologue as in gemm_tern4_kernel.
+    // Prologue: weights of block 0 (then 1 in flight); codes of slabs 0..3 in LDS; trits of
+    // slabs 0 and 1; operands of slab 0 in registers.  The codes and scales are requested
+    // together with the first weights, so the prologue waits for one round trip to memory.
     load_w(wnext, 0);
     load_a(0, 0);
     load_a(1, 1);
@@ -953,7 +679,9 @@ void gemm_tern4w_kernel(LargeArgs args)
 #pragma unroll
     for (int n = 0; n < 8; n++) bf[n] = read_b(0, n);
 
-    // Slab v = 5 blk + d, slots as in gemm_tern4_kernel.  The 32 MFMAs go B tile by B tile
+    // Slab v = 5 blk + d (digit 4 - d of block blk), slots indexed by d: operands of v in
+    // registers, the trits of v + 1 read from slot d + 1, those of v + 2 written to slot
+    // d + 2, the codes of v + 4 requested into slot d + 4 (all mod 5).  The 32 MFMAs go B tile by B tile
     // (MFMA slot 4 n + m is A tile m x B tile n), so B tile n is free once slot 4 n + 3 is
     // issued: its operand of v + 1 is read behind slot 4 n + 5 and has the rest of the slab to
     // arrive.  The A operands of v + 1 go to the other register set (v odd / even), widened
@@ -1079,12 +807,12 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
         return hipErrorInvalidValue;
     if (bits == 4) {
         dim3 grid((N + BN4 - 1) / BN4, (M + BM4 - 1) / BM4, L);
-        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kStates, 8>), grid, dim3(NT4W), 0, stream, a);
-        else if (of.states) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kStates, 4>), grid, dim3(NT4W), 0, stream, a);
-        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kGlu>), grid, dim3(NT4W), 0, stream, a);
-        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kSegments>), grid, dim3(NT4W), 0, stream, a);
-        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4w_kernel<true, kPlain>), grid, dim3(NT4W), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_tern4w_kernel<false, kPlain>), grid, dim3(NT4W), 0, stream, a);
+        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 8>), grid, dim3(NT4), 0, stream, a);
+        else if (of.states) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 4>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern4_kernel<true, kSegments>), grid, dim3(NT4), 0, stream, a);
+        else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern4_kernel<true, kPlain>), grid, dim3(NT4), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_tern4_kernel<false, kPlain>), grid, dim3(NT4), 0, stream, a);
     } else {
         dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, L);
         if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kGlu>), grid, dim3(NT), 0, stream, a);
