@@ -19,7 +19,7 @@
 //     trits of a weight row serve every token row of the tile.  Per slab the codes go from
 //     global memory straight into LDS (buffer loads with the LDS as destination), four slabs
 //     ahead and still packed; every thread turns the next digit of the packed words it holds
-//     into trits for two slabs ahead; each wave issues the 32 MFMAs of the slab from
+//     into trits for three slabs ahead; each wave issues the 32 MFMAs of the slab from
 //     registers and, in their shadow, reads its operands of the next slab -- weight trits and
 //     its own 64 rows of codes, widened in registers.  A short last block keeps its pad
 //     digits (trits 0), so every block has five slabs and slot d of the five LDS slots holds
@@ -653,7 +653,7 @@ void gemm_tern4_kernel(LargeArgs args)
     };
 
     // Prologue: weights of block 0 (then 1 in flight); codes of slabs 0..3 in LDS; trits of
-    // slabs 0 and 1; operands of slab 0 in registers.  The codes and scales are requested
+    // slabs 0, 1 and 2; operands of slab 0 in registers.  The codes and scales are requested
     // together with the first weights, so the prologue waits for one round trip to memory.
     load_w(wnext, 0);
     load_a(0, 0);
@@ -670,6 +670,7 @@ void gemm_tern4_kernel(LargeArgs args)
     take_block(1);
     produce(0);
     produce(1);
+    produce(2);
     wait_vmcnt<1>();                                    // all but block 1's weight load
     block_sync();
     v4i af[2][4], bf[8];                                // A operands of slabs of even / odd index
@@ -680,17 +681,20 @@ void gemm_tern4_kernel(LargeArgs args)
     for (int n = 0; n < 8; n++) bf[n] = read_b(0, n);
 
     // Slab v = 5 blk + d (digit 4 - d of block blk), slots indexed by d: operands of v in
-    // registers, the trits of v + 1 read from slot d + 1, those of v + 2 written to slot
-    // d + 2, the codes of v + 4 requested into slot d + 4 (all mod 5).  The 32 MFMAs go B tile by B tile
+    // registers, the trits of v + 1 read from slot d + 1, those of v + 3 written to slot
+    // d + 3, the codes of v + 4 requested into slot d + 4 (all mod 5).  Writing trits three
+    // slabs ahead lets one workgroup barrier, after every odd slab, serve two slabs: every
+    // write is published by a barrier before its slot is read, and every slot is read before
+    // the barrier that precedes its next write.  The 32 MFMAs go B tile by B tile
     // (MFMA slot 4 n + m is A tile m x B tile n), so B tile n is free once slot 4 n + 3 is
     // issued: its operand of v + 1 is read behind slot 4 n + 5 and has the rest of the slab to
     // arrive.  The A operands of v + 1 go to the other register set (v odd / even), widened
     // from packed tiles read at slot 1.  Slot 0 requests the codes of v + 4; slots 2, 6, 10 and
-    // 14 decode the next digit of the held weight words, written as the trits of v + 2 after
+    // 14 decode the next digit of the held weight words, written as the trits of v + 3 after
     // slot 14; slots 18, 22, 26 and 30 widen the A tiles of v + 1.
     auto slab = [&](int v, int d, auto parity, bool last = false) __attribute__((always_inline)) {
         constexpr int P = decltype(parity)::value, Q = 1 - P;
-        const int s1 = (d + 1) % 5, s2 = (d + 2) % 5, s4 = (d + 4) % 5;
+        const int s1 = (d + 1) % 5, s3 = (d + 3) % 5, s4 = (d + 4) % 5;
         u4 t;
 #pragma unroll
         for (int j = 0; j < 32; j++) {
@@ -698,7 +702,7 @@ void gemm_tern4_kernel(LargeArgs args)
             mfma_acc(acc[m][n], af[P][m], bf[n]);
             // the code request of v + 4, its two instructions half a slab apart
             if (j == 0) {
-                if (d == 3) take_block(v / 5 + 2);    // slab v + 2 opens block v / 5 + 1
+                if (d == 2) take_block(v / 5 + 2);    // slab v + 3 opens block v / 5 + 1
                 load_a_part(v + 4, s4, 0);
             }
             if (j == 16) load_a_part(v + 4, s4, 1);
@@ -707,21 +711,24 @@ void gemm_tern4_kernel(LargeArgs args)
                 for (int i = 0; i < 4; i++) rn[i] = read_a(s1, i);
             }
             if (j == 2 || j == 6 || j == 10 || j == 14) t[j >> 2] = tern_step(pb[j >> 2]);   // at digit 0, pb < 3: q = 0
-            if (j == 14) *reinterpret_cast<u4*>(Bt[s2] + b_lds) = t;
+            if (j == 14) *reinterpret_cast<u4*>(Bt[s3] + b_lds) = t;
             if ((j & 3) == 1 && j >= 5) bf[(j >> 2) - 1] = read_b(s1, (j >> 2) - 1);
             if (j == 18 || j == 22 || j == 26 || j == 30) af[Q][(j - 18) >> 2] = widen(rn[(j - 18) >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
         bf[7] = read_b(s1, 7);
-        // codes of slab v + 2 in LDS before the barrier: issued since, AJ code loads in each of
-        // the last two slabs and one weight load when one of them opened a block
-        if (d >= 3) wait_vmcnt<2 * AJ + 1>();
-        else wait_vmcnt<2 * AJ>();
+        // one barrier per two slabs, after each odd slab: the codes of v + 2 and v + 3 in LDS
+        // before it (issued since: the AJ code loads of this slab and its weight load, if any);
         // after the trit write come, behind scheduling barriers, the B reads of tiles 3..7
-        // (ds_read_b128, which cannot be merged), which may stay in flight -- except in the
-        // last slab of the tile, whose reads of a next slab are dropped as unused
-        if (last) block_sync();
-        else block_sync_reads_in_flight<5>();
+        // (ds_read_b128, which cannot be merged), which may stay in flight.  The tile's last
+        // slab (even) ends with a full barrier: its reads of a next slab are dropped as unused.
+        if (P == 1) {
+            if (d == 2) wait_vmcnt<AJ + 1>();
+            else wait_vmcnt<AJ>();
+            block_sync_reads_in_flight<5>();
+        } else if (last) {
+            block_sync();
+        }
     };
     // Two blocks per iteration, so that the register set of each slab is known at compile
     // time (slab v uses set v & 1); an odd last block starts on an even slab.
