@@ -125,7 +125,10 @@ def test_quantize_rounding_ties(tb, bits):
 # ------------------------------------------------------------------ ternary product ----
 
 GEMM_SHAPES = [(16, 256, 256), (1, 64, 64), (300, 200, 1024), (257, 513, 4096), (64, 64, 320),
-               (33, 17, 960), (512, 256, 16384), (5, 1000, 4032)]
+               (33, 17, 960), (512, 256, 16384), (5, 1000, 4032),
+               # large-M INT4 control flow: two blocks (one loop iteration, no remainder block)
+               # over two ragged M-tiles and N-tiles; one padded block at M just above 16
+               (520, 130, 640), (17, 16, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
