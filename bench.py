@@ -1047,6 +1047,16 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg, rows_max=128 if cfg == 4 else 256)
                     log(f"[bench] {name}: cpu oracle {r['cpu_baseline']['value']:.4g} tokens/s "
                         f"({r['cpu_baseline']['sample']})")
+                    if cfg == 3:
+                        # configurations 1-3 also get the oracle on one thread
+                        nthr = oracle.num_threads()
+                        oracle.set_num_threads(1)
+                        try:
+                            r["cpu_baseline_1thread"] = cpu_baseline_large(si, oracle, cfg, rows_max=16)
+                        finally:
+                            oracle.set_num_threads(nthr)
+                        log(f"[bench] {name}: cpu oracle on one thread "
+                            f"{r['cpu_baseline_1thread']['value']:.4g} tokens/s")
             log(f"[bench] {name}: {r['tokens_per_s']:.4g} tokens/s, gemm {r['gemm_int_tops']:.0f} "
                 f"TOP/s ({100 * r['gemm_mfma_frac']:.1f}% of int8 peak)")
             large[name] = r
