@@ -1044,7 +1044,7 @@ def main():
                 r = run_large(torch, tb, si, cfg, args.large_steps, 2)
                 if not args.no_cpu_baseline and args.only is None:
                     import oracle
-                    r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg, rows_max=128 if cfg == 4 else 256)
+                    r["cpu_baseline"] = cpu_baseline_large(si, oracle, cfg, rows_max=256)
                     log(f"[bench] {name}: cpu oracle {r['cpu_baseline']['value']:.4g} tokens/s "
                         f"({r['cpu_baseline']['sample']})")
                     if cfg == 3:
