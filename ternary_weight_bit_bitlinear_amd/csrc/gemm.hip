@@ -761,6 +761,7 @@ void gemm_tern4_kernel(LargeArgs args)
     mfma_drain();
 
     const float w_scale = args.wscales ? ((const_f32_ptr)(const void*)args.wscales)[layer] : args.wscale0;
+    // this layer's outputs (the SwishGLU and segment forms run one layer)
     void* obase = DEQ ? (void*)(args.out + (int64_t)layer * M * N) : (void*)(args.acc + (int64_t)layer * M * N);
     auto sxf = [&](int fm) __attribute__((always_inline)) {
         return *(const f4*)&sxs[64 * wave + 16 * fm + 4 * g];
@@ -770,7 +771,7 @@ void gemm_tern4_kernel(LargeArgs args)
     if constexpr (EPI == kGlu) {
         if (inside)
             store_tiles_glu_inside<4, 8, 4>(acc, row0, n0, lane, N / 2, sxf, args.of.gate_scale,
-                                            args.of.up_scale, args.out);
+                                            args.of.up_scale, (float*)obase);
         else
             store_tiles_glu<4, 8, 4>(acc, row0, n0, lane, M, N / 2, sxf, args.of.gate_scale,
                                      args.of.up_scale, obase);
@@ -782,12 +783,12 @@ void gemm_tern4_kernel(LargeArgs args)
     else if constexpr (EPI == kSegments) {
         auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
         if (DEQ && inside)
-            store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf, wsf, args.out);
+            store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf, wsf, (float*)obase);
         else
             store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf, wsf, obase);
     } else if (DEQ && inside)
         store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf,
-                                    [&](int) __attribute__((always_inline)) { return w_scale; }, args.out);
+                                    [&](int) __attribute__((always_inline)) { return w_scale; }, (float*)obase);
     else
         store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf,
                                   [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
