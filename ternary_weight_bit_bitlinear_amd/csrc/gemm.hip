@@ -125,6 +125,14 @@ __device__ __forceinline__ void mfma_acc(v4i& acc, const v4i& a, const v4i& b)
     asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Wait states between a vector instruction that writes an MFMA operand and the MFMA that reads
+// it (the MFMAs are inline asm, so the compiler inserts none).  The operand is an input of the
+// asm, so the instructions that write it cannot be moved below the wait.
+__device__ __forceinline__ void mfma_operand_wait(const v4i& x)
+{
+    asm volatile("s_nop 4" :: "v"(x) : "memory");
+}
+
 // Wait states between the last MFMA and the first read of its result by other instructions
 // (more than the longest MFMA latency).
 __device__ __forceinline__ void mfma_drain()
@@ -567,7 +575,19 @@ void gemm_tern4_kernel(LargeArgs args)
         return s == 0 ? A0 : s == 1 ? A1 : s == 2 ? A2 : s == 3 ? A3 : A4;
     };
 
-    const int layer = blockIdx.z;
+    // Tile order: workgroups are dispatched to the 8 XCDs in turn (linear index mod 8); XCD j
+    // takes a contiguous run of the tiles in (layer, row block, column block) order, so that the
+    // workgroups resident on one XCD at a time share their activation rows in that XCD's L2.
+    int layer, tile_y, tile_x;
+    {
+        const int gx = gridDim.x, gy = gridDim.y, total = gx * gy * gridDim.z;
+        const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+        const int xcd = id & 7, q = total >> 3, r = total & 7;
+        const int p = xcd * q + (xcd < r ? xcd : r) + (id >> 3);
+        tile_x = p % gx;
+        tile_y = (p / gx) % gy;
+        layer = p / (gx * gy);
+    }
     const int M = args.M, N = args.N, K = args.K;
     const int crow = K / 2;
     const uint8_t* codes = args.codes + (int64_t)layer * M * crow;
@@ -575,7 +595,7 @@ void gemm_tern4_kernel(LargeArgs args)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int m0 = tile_y * BM, n0 = tile_x * BN;
     const int nblk = (K + 319) / 320;
     const int groups = (N + 15) / 16;
 
@@ -734,8 +754,13 @@ void gemm_tern4_kernel(LargeArgs args)
     // time (slab v uses set v & 1); an odd last block starts on an even slab.
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    // The other forms run the tile's last block separately (below) and store each A tile row's
+    // outputs while the next row computes; the states form, whose epilogue per row is large,
+    // runs every block here and stores after the last one.
+    constexpr bool FB = EPI != kStates;
+    const int nbb = FB ? nblk - 1 : nblk;
     int blk = 0;
-    for (; blk + 1 < nblk; blk += 2) {
+    for (; blk + 1 < nbb; blk += 2) {
         const int v = 5 * blk;
         slab(v, 0, P0{});
         slab(v + 1, 1, P1{});
@@ -748,50 +773,107 @@ void gemm_tern4_kernel(LargeArgs args)
         slab(v + 8, 3, P0{});
         slab(v + 9, 4, P1{});
     }
-    if (blk < nblk) {
+    if (blk < nbb) {
         const int v = 5 * blk;
         slab(v, 0, P0{});
         slab(v + 1, 1, P1{});
         slab(v + 2, 2, P0{});
         slab(v + 3, 3, P1{});
-        slab(v + 4, 4, P0{}, true);
+        slab(v + 4, 4, P0{}, !FB);
     }
-
-    wait_vmcnt<0>();
-    mfma_drain();
 
     const float w_scale = args.wscales ? ((const_f32_ptr)(const void*)args.wscales)[layer] : args.wscale0;
     // this layer's outputs (the SwishGLU and segment forms run one layer)
     void* obase = DEQ ? (void*)(args.out + (int64_t)layer * M * N) : (void*)(args.acc + (int64_t)layer * M * N);
-    auto sxf = [&](int fm) __attribute__((always_inline)) {
-        return *(const f4*)&sxs[64 * wave + 16 * fm + 4 * g];
-    };
     const int row0 = m0 + 64 * wave;
-    const bool inside = row0 + 64 <= M && n0 + 128 <= N;
-    if constexpr (EPI == kGlu) {
-        if (inside)
-            store_tiles_glu_inside<4, 8, 4>(acc, row0, n0, lane, N / 2, sxf, args.of.gate_scale,
-                                            args.of.up_scale, (float*)obase);
+    // The outputs of A tile row fm (16 token rows x 128 outputs), in the tile's output form.
+    auto epilogue_row = [&](int fm) __attribute__((always_inline)) {
+        v4i ar[1][8];
+#pragma unroll
+        for (int n = 0; n < 8; n++) ar[0][n] = acc[fm][n];
+        const int r0 = row0 + 16 * fm;
+        const bool inside = r0 + 16 <= M && n0 + 128 <= N;
+        auto sxf = [&](int) __attribute__((always_inline)) {
+            return *(const f4*)&sxs[64 * wave + 16 * fm + 4 * g];
+        };
+        if constexpr (EPI == kGlu) {
+            if (inside)
+                store_tiles_glu_inside<1, 8, 4>(ar, r0, n0, lane, N / 2, sxf, args.of.gate_scale,
+                                                args.of.up_scale, (float*)obase);
+            else
+                store_tiles_glu<1, 8, 4>(ar, r0, n0, lane, M, N / 2, sxf, args.of.gate_scale,
+                                         args.of.up_scale, obase);
+        } else if constexpr (EPI == kSegments) {
+            auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
+            if (DEQ && inside)
+                store_tiles_inside<1, 8, 4>(ar, r0, n0, lane, N, sxf, wsf, (float*)obase);
+            else
+                store_tiles<1, 8, 4, DEQ>(ar, r0, n0, lane, M, N, sxf, wsf, obase);
+        } else if (DEQ && inside)
+            store_tiles_inside<1, 8, 4>(ar, r0, n0, lane, N, sxf,
+                                        [&](int) __attribute__((always_inline)) { return w_scale; }, (float*)obase);
         else
-            store_tiles_glu<4, 8, 4>(acc, row0, n0, lane, M, N / 2, sxf, args.of.gate_scale,
-                                     args.of.up_scale, obase);
-    } else if constexpr (EPI == kStates)
+            store_tiles<1, 8, 4, DEQ>(ar, r0, n0, lane, M, N, sxf,
+                                      [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
+    };
+
+    // The last block (slabs v0 .. v0 + 4 in slots 0 .. 4): its codes and trits all in LDS at
+    // once, the MFMAs A tile row by A tile row (step 5 m + d: row m x slab d), so that the
+    // outputs of row m leave while row m + 1 runs: they are stored after the first four MFMAs
+    // of row m + 1, well past the latency of row m's last MFMA.  Operands are read one step
+    // ahead into the other register set.  Slot 4's codes, requested here, are waited for at
+    // step 4; slot 4 and trit slots 3 and 4 are free once every wave's reads have completed.
+    if constexpr (FB) {
+        const int v0 = 5 * nbb;
+        // every wave's reads of the slots written below have landed (the last barrier may have
+        // been a relaxed one, with a wave's last B reads -- of trit slot 4 -- still in flight)
+        block_sync();
+        load_a(v0 + 4, 4);
+        produce(3);                                     // at digit 0, pb < 3: q = 0
+        produce(4);
+        wait_vmcnt<AJ>();                               // every code load but those of slot 4
+        block_sync();
+        v4i fa[2], fbv[2][8];
+        ARaw fr;
+        fa[0] = widen(read_a(0, 0));
+#pragma unroll
+        for (int n = 0; n < 8; n++) fbv[0][n] = read_b(0, n);
+        mfma_operand_wait(fa[0]);
+#pragma unroll
+        for (int st = 0; st < 20; st++) {
+            const int m = st / 5, d = st % 5, cur = st & 1, nxt = cur ^ 1;
+            const int sn = st + 1, mn = sn / 5, dn = sn % 5;
+            if (st == 4) {
+                wait_vmcnt<0>();                        // the codes of slot 4
+                block_sync();
+                fa[cur] = widen(read_a(4, 0));
+                mfma_operand_wait(fa[cur]);
+            }
+            const bool pre = sn < 20 && !(dn == 4 && mn == 0);   // slot 4's codes of row 0: after step 4's barrier
+            if (pre) fr = read_a(dn, mn);
+#pragma unroll
+            for (int n = 0; n < 8; n++) {
+                mfma_acc(acc[m][n], fa[cur], fbv[cur][n]);
+                if (sn < 20) fbv[nxt][n] = read_b(dn, n);
+                if (n == 3 && d == 0 && m >= 1) epilogue_row(m - 1);
+                if (n == 4 && pre) fa[nxt] = widen(fr);   // three MFMAs before its first reader
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    mfma_drain();
+    if constexpr (FB) {
+        epilogue_row(3);
+    } else {
+        auto sxf = [&](int fm) __attribute__((always_inline)) {
+            return *(const f4*)&sxs[64 * wave + 16 * fm + 4 * g];
+        };
         store_tiles_states<4, 8, 4, SG>(acc, row0, n0, lane, M, N, sxf,
                                         [&](int fn) __attribute__((always_inline)) {
                                             return group_scale(args.of, n0 / 16 + fn, w_scale);
                                         }, args.of, (void*)args.out);
-    else if constexpr (EPI == kSegments) {
-        auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, n0 / 16 + fn, w_scale); };
-        if (DEQ && inside)
-            store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf, wsf, (float*)obase);
-        else
-            store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf, wsf, obase);
-    } else if (DEQ && inside)
-        store_tiles_inside<4, 8, 4>(acc, row0, n0, lane, N, sxf,
-                                    [&](int) __attribute__((always_inline)) { return w_scale; }, (float*)obase);
-    else
-        store_tiles<4, 8, 4, DEQ>(acc, row0, n0, lane, M, N, sxf,
-                                  [&](int) __attribute__((always_inline)) { return w_scale; }, obase);
+    }
 }
 
 }  // namespace

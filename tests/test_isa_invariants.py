@@ -57,3 +57,53 @@ def test_relaxed_barriers_follow_enough_lds_reads(tmp_path):
                 if m and int(m.group(1)) > 0:
                     pending = (after_write, reads, int(m.group(1)))
     assert seen >= 4 * 5
+
+
+def _vregs(tok):
+    """VGPR numbers named by an operand such as v7 or v[12:15] (AGPRs and SGPRs give none)."""
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return range(int(m.group(1)), int(m.group(2)) + 1)
+    m = re.fullmatch(r"v(\d+)", tok)
+    return range(int(m.group(1)), int(m.group(1)) + 1) if m else range(0)
+
+
+@pytest.mark.skipif(hipcc() is None, reason="hipcc needed")
+def test_mfma_operands_settle_before_use(tmp_path):
+    """The MFMAs are inline asm, so the compiler inserts no wait states between a vector
+    instruction that writes an A or B operand register and the MFMA that reads it; the source
+    places them (or an s_nop that takes the operand as input).  Within each basic block, every
+    MFMA must find its operand registers last written by a vector instruction at least five
+    wait states earlier (one per instruction, N + 1 per s_nop N)."""
+    out = tmp_path / "gemm.s"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "gemm.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    kernels = re.split(r"\n(?=_ZN\S*gemm_tern\w*_kernel\S*:)", text)[1:]
+    assert len(kernels) >= 6
+    need, checked = 5, 0
+    for k in kernels:
+        body = k.split(".Lfunc_end", 1)[0]
+        name = body.split(":", 1)[0]
+        clock, written = 0, {}
+        for line in body.splitlines()[1:]:
+            s = line.split(";", 1)[0].strip()
+            if not s or s.startswith("."):
+                if s.startswith(".LBB"):
+                    written = {}                        # a block boundary: start afresh
+                continue
+            op, _, rest = s.partition(" ")
+            ops = [t.strip() for t in rest.split(",")]
+            if op.startswith("v_mfma"):
+                for src in ops[1:3]:
+                    for r in _vregs(src):
+                        if r in written:
+                            assert clock - written[r] >= need, f"{name}: v{r} written {clock - written[r]} wait states before {s}"
+                checked += 1
+            elif op.startswith("v_") and ops:
+                for r in _vregs(ops[0]):
+                    written[r] = clock
+            clock += int(ops[0], 0) + 1 if op == "s_nop" else 1
+    assert checked >= 4 * 640
