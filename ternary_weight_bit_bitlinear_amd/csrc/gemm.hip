@@ -94,6 +94,7 @@ struct LargeArgs {
     int32_t* acc;                  // L x M x N int32, or null
     int M, K, N;
     OutForm of;                    // segments / gate-up pairs (L = 1, out only)
+    int xcd_runs;                  // INT4 kernel: tile order by XCD runs (else launch order)
 };
 
 // Workgroup barrier after this wave's LDS operations have completed.  Written out (rather
@@ -575,11 +576,13 @@ void gemm_tern4_kernel(LargeArgs args)
         return s == 0 ? A0 : s == 1 ? A1 : s == 2 ? A2 : s == 3 ? A3 : A4;
     };
 
-    // Tile order: workgroups are dispatched to the 8 XCDs in turn (linear index mod 8); XCD j
-    // takes a contiguous run of the tiles in (layer, row block, column block) order, so that the
-    // workgroups resident on one XCD at a time share their activation rows in that XCD's L2.
-    int layer, tile_y, tile_x;
-    {
+    // Tile order: workgroups are dispatched to the 8 XCDs in turn (linear index mod 8).  With
+    // xcd_runs, XCD j takes a contiguous run of the tiles in (layer, row block, column block)
+    // order, so that the workgroups resident on one XCD at a time share their activation rows
+    // in that XCD's L2; the launcher asks for it when the tiles take more than one round of the
+    // CUs (a single round measured faster in launch order).
+    int layer = blockIdx.z, tile_y = blockIdx.y, tile_x = blockIdx.x;
+    if (args.xcd_runs) {
         const int gx = gridDim.x, gy = gridDim.y, total = gx * gy * gridDim.z;
         const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
         const int xcd = id & 7, q = total >> 3, r = total & 7;
@@ -691,7 +694,9 @@ void gemm_tern4_kernel(LargeArgs args)
     produce(0);
     produce(1);
     produce(2);
-    wait_vmcnt<1>();                                    // all but block 1's weight load
+    // the codes of slabs 0..2 (slab 1 reads those of slab 2); slab 3's, the scales and block
+    // 1's weights may stay in flight: the barrier after slab 1 waits for slab 3's codes
+    wait_vmcnt<AJ + NSX + 1>();
     block_sync();
     v4i af[2][4], bf[8];                                // A operands of slabs of even / odd index
     ARaw rn[4];                                         // packed A tiles of the next slab
@@ -878,6 +883,19 @@ void gemm_tern4_kernel(LargeArgs args)
 
 }  // namespace
 
+// Compute units of the current device, queried once per device (256 on MI355X).
+static int device_cu_count()
+{
+    static int count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (count[dev] <= 0) {
+        int n = 0;
+        count[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    }
+    return count[dev];
+}
+
 hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, int bits,
                              const uint8_t* const* wptrs, const uint8_t* w0,
                              const float* scales, const float* wscales, float wscale0,
@@ -891,12 +909,13 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
     if (packed >= ((int64_t)1 << 31) || (int64_t)M * crow >= ((int64_t)1 << 31) ||
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
-    LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N, of};
+    LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N, of, 0};
     if (of.states && (bits != 4 || L != 1 || out_f32 == nullptr || of.nseg == 0 ||
                       (of.state_tiles != 4 && of.state_tiles != 8) || N % (16 * of.state_tiles) != 0))
         return hipErrorInvalidValue;
     if (bits == 4) {
         dim3 grid((N + BN4 - 1) / BN4, (M + BM4 - 1) / BM4, L);
+        a.xcd_runs = (int64_t)grid.x * grid.y * grid.z > device_cu_count();
         if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 8>), grid, dim3(NT4), 0, stream, a);
         else if (of.states) hipLaunchKernelGGL((gemm_tern4_kernel<true, kStates, 4>), grid, dim3(NT4), 0, stream, a);
         else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern4_kernel<true, kGlu>), grid, dim3(NT4), 0, stream, a);

@@ -128,7 +128,10 @@ GEMM_SHAPES = [(16, 256, 256), (1, 64, 64), (300, 200, 1024), (257, 513, 4096), 
                (33, 17, 960), (512, 256, 16384), (5, 1000, 4032),
                # large-M INT4 control flow: two blocks (one loop iteration, no remainder block)
                # over two ragged M-tiles and N-tiles; one padded block at M just above 16
-               (520, 130, 640), (17, 16, 64)]
+               (520, 130, 640), (17, 16, 64),
+               # 17 x 17 = 289 tiles of 512 x 128, more than one round of the CUs: the INT4
+               # kernel's tile order by XCD runs, over a tile count that is not a multiple of 8
+               (8193, 2176, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)

@@ -72,9 +72,11 @@ def _vregs(tok):
 def test_mfma_operands_settle_before_use(tmp_path):
     """The MFMAs are inline asm, so the compiler inserts no wait states between a vector
     instruction that writes an A or B operand register and the MFMA that reads it; the source
-    places them (or an s_nop that takes the operand as input).  Within each basic block, every
-    MFMA must find its operand registers last written by a vector instruction at least five
-    wait states earlier (one per instruction, N + 1 per s_nop N)."""
+    places them (or an s_nop that takes the operand as input).  Every MFMA must find its operand
+    registers last written by a vector instruction at least five wait states earlier (one per
+    instruction, N + 1 per s_nop N), counted in layout order through block labels: conservative
+    where a branch skips code, and it also sees a write that the compiler sank past a branch
+    into the block of its MFMA."""
     out = tmp_path / "gemm.s"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
@@ -91,8 +93,6 @@ def test_mfma_operands_settle_before_use(tmp_path):
         for line in body.splitlines()[1:]:
             s = line.split(";", 1)[0].strip()
             if not s or s.startswith("."):
-                if s.startswith(".LBB"):
-                    written = {}                        # a block boundary: start afresh
                 continue
             op, _, rest = s.partition(" ")
             ops = [t.strip() for t in rest.split(",")]
