@@ -344,7 +344,10 @@ def test_forward_rejects_small_workspace(tb):
 @pytest.mark.parametrize("L,M,K,N,bits,had", [(5, 16, 4096, 512, 8, False), (3, 1, 1024, 300, 8, True),
                                               (4, 40, 4096, 256, 4, True), (2, 7, 960, 100, 4, False),
                                               # tiles whose rows and columns all lie inside the output
-                                              (3, 600, 1024, 384, 4, True), (2, 300, 640, 272, 8, False)])
+                                              (3, 600, 1024, 384, 4, True), (2, 300, 640, 272, 8, False),
+                                              # 2 x 9 x 17 = 306 INT4 tiles, more than one round of the
+                                              # CUs: the tile order by XCD runs across two layers
+                                              (2, 4196, 640, 2112, 4, False)])
 def test_forward_grouped_matches_oracle(tb, L, M, K, N, bits, had):
     say(f"  grouped L={L} M={M} K={K} N={N} bits={bits} had={had}")
     x = si.normal(si.seed_for(8, 0) + K + M, L * M * K).reshape(L, M, K)
