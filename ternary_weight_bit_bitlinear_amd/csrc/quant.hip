@@ -79,11 +79,15 @@ __host__ __device__ constexpr int num_groups(int L, int LE) { return 1 + (L - 2 
 // two lanes that differ in bit 7 of k meet in one bank (1-6 % slower at K = 4096..16384;
 // K = 1024 measured faster with the narrower form).  Either form is its own inverse on [0, K).
 template <int L>
-__device__ __forceinline__ uint32_t swz(uint32_t k)
+__host__ __device__ constexpr uint32_t swz(uint32_t k)
 {
     if constexpr (L >= 12) return k ^ (((k >> 7) & 15u) << 2);
     else return k ^ (((k >> 8) & 7u) << 2);
 }
+
+// Index bits that swz can change (bits 2..5, or 2..4 below K = 4096).
+template <int L>
+__host__ __device__ constexpr uint32_t swz_bits() { return L >= 12 ? 15u << 2 : 7u << 2; }
 
 // Position of index bit b among the register bits of MASK.
 __host__ __device__ constexpr int regpos(uint32_t mask, int b)
@@ -136,36 +140,49 @@ __device__ __forceinline__ uint32_t thread_bits(uint32_t t)
     return pdep(t, ((1u << L) - 1u) & ~MASK);
 }
 
+// LDS byte address of register e of layout MASK.  swz is linear over XOR and the thread part
+// tb and register part of k have no bit in common, so swz(k) = swz(tb) ^ swz(ke); the two
+// parts can share only bits that swz changes, so swz(k) = (swz(tb) ^ lo) + hi with lo the
+// register part's share of those bits and hi the rest.  tb4 = 4 swz(tb) is formed once per
+// thread; each distinct lo costs one XOR and hi becomes the instruction's immediate offset.
+template <int L, uint32_t MASK>
+__device__ __forceinline__ uint32_t layout_addr(uint32_t tb4, int e)
+{
+    const uint32_t c = swz<L>(pdep((uint32_t)e, MASK));
+    const uint32_t lo = c & swz_bits<L>(), hi = c & ~swz_bits<L>();
+    return (tb4 ^ (lo << 2)) + (hi << 2);
+}
+
 template <int L, uint32_t MASK, int E>
 __device__ __forceinline__ void store_layout(float* lds, uint32_t t, const float (&v)[E])
 {
-    const uint32_t tb = thread_bits<L, MASK>(t);
+    const uint32_t tb4 = swz<L>(thread_bits<L, MASK>(t)) << 2;
+    char* base = reinterpret_cast<char*>(lds);
     if constexpr ((MASK & 3u) == 3u) {
 #pragma unroll
-        for (int e = 0; e < E; e += 4) {
-            uint32_t k = tb | pdep((uint32_t)e, MASK);
-            *reinterpret_cast<float4*>(lds + swz<L>(k)) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
-        }
+        for (int e = 0; e < E; e += 4)
+            *reinterpret_cast<float4*>(base + layout_addr<L, MASK>(tb4, e)) =
+                make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
     } else {
 #pragma unroll
-        for (int e = 0; e < E; e++) lds[swz<L>(tb | pdep((uint32_t)e, MASK))] = v[e];
+        for (int e = 0; e < E; e++) *reinterpret_cast<float*>(base + layout_addr<L, MASK>(tb4, e)) = v[e];
     }
 }
 
 template <int L, uint32_t MASK, int E>
 __device__ __forceinline__ void load_layout(const float* lds, uint32_t t, float (&v)[E])
 {
-    const uint32_t tb = thread_bits<L, MASK>(t);
+    const uint32_t tb4 = swz<L>(thread_bits<L, MASK>(t)) << 2;
+    const char* base = reinterpret_cast<const char*>(lds);
     if constexpr ((MASK & 3u) == 3u) {
 #pragma unroll
         for (int e = 0; e < E; e += 4) {
-            uint32_t k = tb | pdep((uint32_t)e, MASK);
-            float4 f = *reinterpret_cast<const float4*>(lds + swz<L>(k));
+            float4 f = *reinterpret_cast<const float4*>(base + layout_addr<L, MASK>(tb4, e));
             v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < E; e++) v[e] = lds[swz<L>(tb | pdep((uint32_t)e, MASK))];
+        for (int e = 0; e < E; e++) v[e] = *reinterpret_cast<const float*>(base + layout_addr<L, MASK>(tb4, e));
     }
 }
 
