@@ -794,6 +794,56 @@ def run_qkv_states(torch, tb, si, steps):
     return res
 
 
+def run_qkv_states_decode(torch, tb, si, steps, M=16):
+    """The block's Q, K and V projections at a decode step (M = 16 tokens, K = 4096, one
+    three-segment launch of the decode kernel) with the low-bit states in the epilogue -- the
+    rows a 3-bit KV cache takes on each step -- against the same launch writing fp32, with
+    INT8 and INT4 activations."""
+    import numpy as np
+    wl = si.workload(5, M=M)                  # the block's first M token rows
+    L = {l.name: l for l in wl.linears}
+    K = L["q"].K
+    seg_n = [L[n].N for n in ("q", "k", "v")]
+    N = sum(seg_n)
+    bits, group = [4, 3, 3], 128
+    x = torch.from_numpy(si.activations(5, L["q"])).cuda()
+    W = np.concatenate([si.weights(5, L[n]) for n in ("q", "k", "v")])
+    packed, gs = tb.bitnet_pack_weights_segments(W, seg_n)
+    del W
+    pw = torch.from_numpy(packed).cuda()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    sc = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    ss = torch.empty((M, N // group), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    wbytes = canonical_packed_bytes(N, K)
+    res = dict(workload=f"bitnet_v2_qkv_states_decode_M{M}_K{K}", M=M, K=K, seg_n=seg_n,
+               state_bits=bits, group=group, packed_weight_bytes=wbytes)
+    for act in (8, 4):
+        codes, scales = tb.hbitlinear_quantize(x, act, False)
+        for mode in ("fp32", "states"):
+            def once():
+                if mode == "fp32":
+                    tb.hbitlinear_gemm_dequant_segments(codes, scales, M, K, seg_n, act, pw, gs, out=y,
+                                                        stream=stream)
+                else:
+                    tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, act, pw, gs, bits, group,
+                                                  state_codes=sc, state_scales=ss, stream=stream)
+            for _ in range(3):
+                once()
+            torch.cuda.synchronize()
+            t = Timer(torch, steps)
+            for _ in range(steps):
+                t.begin(stream)
+                once()
+                t.end(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * t.mean_ms()
+            res[f"a{act}_{mode}"] = dict(launch_us=us, weight_gbs=wbytes / (us * 1e-6) / 1e9)
+    del x, y, sc, ss, pw
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_k1_rmsnorm(torch, tb, si, steps):
     """The activation stage with and without the RMS norm folded in, at the large-M shapes: the
     norm adds a reduction and a gain read but no pass over x."""
@@ -1064,6 +1114,9 @@ def main():
             large["qkv_states"] = r = run_qkv_states(torch, tb, si, args.large_steps)
             log(f"[bench] qkv states: fp32 out {r['fp32']['launch_us']:.1f} us, states fused "
                 f"{r['states']['launch_us']:.1f} us")
+            large["qkv_states_decode"] = r = run_qkv_states_decode(torch, tb, si, 50)
+            log(f"[bench] qkv states at M = {r['M']}: " + ", ".join(
+                f"{k} {v['launch_us']:.1f} us" for k, v in r.items() if isinstance(v, dict)))
         if args.only is None:
             log("[bench] activation stage with the RMS norm folded in")
             large["k1_rmsnorm"] = run_k1_rmsnorm(torch, tb, si, 20)

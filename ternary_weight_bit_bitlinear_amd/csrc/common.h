@@ -78,6 +78,24 @@ __device__ inline float silu_mul(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Maximum over the 16 lanes 16 i .. 16 i + 15 that share an MFMA 16x16 output row group, by
+// DPP moves inside the row of 16 lanes: swap neighbours, swap pairs, mirror the halves of
+// eight, mirror the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+    return v;
+}
+
 // Internal launchers (quant.hip, gemm.hip).  Arguments are validated by the caller.
 // gain != nullptr: RMS-normalise each row first (gain: K fp32, device; eps >= 0); K must then
 // be a power of two in [256, 16384].

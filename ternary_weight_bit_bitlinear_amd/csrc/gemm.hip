@@ -283,24 +283,6 @@ __device__ __forceinline__ void store_tiles_glu(const v4i (&acc)[FM][FN], int ro
     }
 }
 
-// Maximum over the 16 lanes 16 i .. 16 i + 15 that share this lane's MFMA output rows, by
-// DPP moves inside the row of 16 lanes: swap neighbours, swap pairs, mirror the halves of
-// eight, mirror the row.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xF, 0xF, false));
-}
-__device__ __forceinline__ float max16(float v)
-{
-    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1, 0, 3, 2]
-    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2, 3, 0, 1]
-    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
-    return v;
-}
-
 // Low-bit Q/K/V states (BitNet v2 write-up: QKV states at reduced bit widths, zero-shot
 // tables 2 and 3; a 3-bit KV cache): each output y, dequantised as in store_tiles, is
 // quantised per row and per group of 16 TG consecutive columns (one attention head) with its
@@ -937,7 +919,6 @@ hipError_t launch_gemm(const uint8_t* codes, int L, int M, int K, int N, int bit
                        const float* wscales, float wscale0, float* out_f32, int32_t* acc_i32,
                        hipStream_t stream, const OutForm& of)
 {
-    if (of.states && M <= 16) return hipErrorInvalidValue;   // the decode kernels have no states form
     if (M <= 16)
         return launch_gemm_decode(codes, L, M, K, N, bits, wptrs, w0, scales, wscales, wscale0,
                                   out_f32, acc_i32, stream, of);

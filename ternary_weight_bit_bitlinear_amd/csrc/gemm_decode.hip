@@ -198,16 +198,18 @@ struct StreamPos {
 
 // Epilogue forms of the streaming kernel, one instantiation each, so that the plain one carries
 // none of the others' code inside its loop: one weight scale per layer; a scale per row
-// segment; gate / up pairs.
-enum Epi { kPlain = 0, kSegments = 1, kGlu = 2 };
+// segment; gate / up pairs; segments whose outputs leave as low-bit states (SG tiles of 16
+// columns per head).
+enum Epi { kPlain = 0, kSegments = 1, kGlu = 2, kStates = 3 };
 
-template <int BITS, bool DEQ, int TPW, int EPI = kPlain>
+template <int BITS, bool DEQ, int TPW, int EPI = kPlain, int SG = 0>
 __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
 {
     constexpr int WAVE_ROWS = 16 * TPW, WG_ROWS = wg_rows(TPW);
     __shared__ __align__(16) uint32_t lut[256 * 64];   // 256 values x 32 copies x 8 bytes
     __shared__ __align__(16) uint8_t abuf[2][16 * ASTRIDE];
     __shared__ float sbuf[2][17];     // activation scales of the 16 rows, then the weight scale
+    __shared__ float sred[EPI == kStates ? 4 * 16 : 1];   // states: a wave's head maxima per row
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     build_table(lut, tid);
@@ -342,6 +344,75 @@ __global__ __launch_bounds__(DT, 2) void gemm_decode_kernel(DecodeArgs a)
     auto finish = [&](const StreamPos& p, int buf) {
         const float wsc = DEQ ? sbuf[buf][16] : 0.0f;
         const int row0 = p.c * WG_ROWS + wave * WAVE_ROWS;
+        if constexpr (EPI == kStates) {
+            // Low-bit states, as the large-M kernel's store_tiles_states: each output y,
+            // dequantised as below, is quantised per row and per head of 16 SG columns with its
+            // segment's Qp.  A head is WPH = SG / TPW consecutive waves of the workgroup (the
+            // launcher takes TPW = SG / 4: one head per workgroup): the head's maximum for a row
+            // is the lane's maximum over its tiles, then over the 16 lanes of the row group
+            // (max16), then over the head's waves through LDS.  Every wave reaches this point at
+            // the same step, so the barrier is met by all.
+            constexpr int WPH = SG / TPW;
+            static_assert(DEQ && (SG == 4 || SG == 8) && SG % TPW == 0 && (WPH == 1 || WPH == 2 || WPH == 4),
+                          "states: fp32 epilogue, a head within one workgroup");
+            const int nheads = N / (16 * SG), head = row0 / (16 * SG);
+            const int qp = group_qp(a.of, row0 / 16);
+            float wsv[TPW];
+#pragma unroll
+            for (int f = 0; f < TPW; f++) wsv[f] = group_scale(a.of, row0 / 16 + f, wsc);
+            float y[TPW][4], amax[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float sx = sbuf[buf][4 * g + r];
+                float m = 0.0f;
+#pragma unroll
+                for (int f = 0; f < TPW; f++) {
+                    y[f][r] = ((float)acc[f][r] * sx) * wsv[f];
+                    m = fmaxf(m, fabsf(y[f][r]));
+                }
+                amax[r] = max16(m);
+            }
+            if constexpr (WPH > 1) {
+                if ((lane & 15) == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sred[16 * wave + 4 * g + r] = amax[r];
+                }
+                __syncthreads();
+                const int w0 = wave & ~(WPH - 1);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    float m = sred[16 * w0 + 4 * g + r];
+#pragma unroll
+                    for (int w = 1; w < WPH; w++) m = fmaxf(m, sred[16 * (w0 + w) + 4 * g + r]);
+                    amax[r] = m;
+                }
+            }
+            const auto cs = __builtin_amdgcn_make_buffer_rsrc((void*)a.out, 0, M * N, 0x00020000);
+            const auto ss = __builtin_amdgcn_make_buffer_rsrc((void*)a.of.state_scales, 0, 4 * M * nheads,
+                                                              0x00020000);
+            const bool owner = (lane & 15) == 0 && wave % WPH == 0;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int mo = 4 * g + r;
+                const float inv = amax[r] > 0.0f ? (float)qp / amax[r] : 0.0f;   // IEEE division
+#pragma unroll
+                for (int f = 0; f < TPW; f++) {
+                    const int n = row0 + 16 * f + (lane & 15);
+                    int q = (int)__builtin_rintf(y[f][r] * inv);              // round half to even
+                    q = q > qp ? qp : (q < -qp - 1 ? -qp - 1 : q);
+                    const uint32_t o = mo < M && n < N ? (uint32_t)(mo * N + n) : 0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q, cs, (int)o, 0, kNonTemporal);
+                }
+                const float sc = amax[r] > 0.0f ? amax[r] / (float)qp : 0.0f;
+                const uint32_t so = owner && mo < M && head < nheads ? 4u * (uint32_t)(mo * nheads + head)
+                                                                     : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ss, (int)so, 0,
+                                                      kNonTemporal);
+            }
+#pragma unroll
+            for (int f = 0; f < TPW; f++) acc[f] = v4i{0, 0, 0, 0};
+            return;
+        }
         if constexpr (EPI == kGlu) {
             static_assert(DEQ && TPW % 2 == 0, "gate / up pairs need the fp32 epilogue and tile pairs");
             {
@@ -603,7 +674,11 @@ void launch_decode(DecodeKind kind, int grid, const DecodeArgs& a, hipStream_t s
     if (kind == DecodeKind::SplitK)
         hipLaunchKernelGGL((gemm_decode_splitk_kernel<BITS, DEQ>), dim3(grid), dim3(DT), 0, stream, a);
     else if constexpr (DEQ) {
-        if (a.of.glu) launch_streaming<BITS, DEQ, kGlu>(kind, grid, a, stream);
+        if (a.of.states && a.of.state_tiles == 8)   // one head of 128 per workgroup
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 2, kStates, 8>), dim3(grid), dim3(DT), 0, stream, a);
+        else if (a.of.states)                       // one head of 64 per workgroup
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, DEQ, 1, kStates, 4>), dim3(grid), dim3(DT), 0, stream, a);
+        else if (a.of.glu) launch_streaming<BITS, DEQ, kGlu>(kind, grid, a, stream);
         else if (a.of.nseg > 0) launch_streaming<BITS, DEQ, kSegments>(kind, grid, a, stream);
         else launch_streaming<BITS, DEQ, kPlain>(kind, grid, a, stream);
     } else {
@@ -640,8 +715,10 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     DecodeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, L, M, K, N, of};
-    // Enough 256-row items to give every CU one: the streaming kernel with four tiles per wave.
-    // Else, for gate / up pairs, the streaming kernel with two tiles per wave (128-row items).
+    // Low-bit states: the streaming kernel with one head per workgroup (items of the head's 64
+    // or 128 rows, one or two tiles per wave).  Else, enough 256-row items to give every CU
+    // one: the streaming kernel with four tiles per wave.  Else, for gate / up pairs, the
+    // streaming kernel with two tiles per wave (128-row items).
     // Else, when the 16-row groups fit two workgroups per CU: one workgroup per group, K split
     // over its waves.  Else the streaming kernel with one tile per wave (64-row items).
     const int cus = device_cus();
@@ -649,7 +726,14 @@ hipError_t launch_gemm_decode(const uint8_t* codes, int L, int M, int K, int N, 
     const int groups = L * ((N + 15) / 16);
     DecodeKind kind;
     int grid;
-    if (items4 >= cus) {
+    if (of.states && (out_f32 == nullptr || L != 1 || (of.state_tiles != 4 && of.state_tiles != 8) ||
+                      N % (16 * of.state_tiles) != 0))
+        return hipErrorInvalidValue;
+    if (of.states) {
+        kind = DecodeKind::Wide;                 // the kind is not used for states
+        const int itemsh = L * ((N + 16 * of.state_tiles - 1) / (16 * of.state_tiles));
+        grid = itemsh < 2 * cus ? itemsh : 2 * cus;
+    } else if (items4 >= cus) {
         kind = DecodeKind::Wide;
         grid = items4 < 2 * cus ? items4 : 2 * cus;
     } else if (of.glu) {

@@ -799,6 +799,39 @@ def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had):
     np.testing.assert_array_equal(ss.cpu().numpy()[match], os_[match])
 
 
+# The states form of the decode kernel (M <= 16, INT8 or INT4 activations, always the
+# streaming kernel with four column tiles per wave): heads of 64 columns (one wave's tiles) and
+# of 128 (two waves, their maxima combined through LDS), segment boundaries inside a
+# workgroup's 256 columns, a workgroup past the last column, a zero row, and the width of the
+# block's Q/K/V projections; every row and column against the oracle run on the GPU's own
+# activation codes (bit-identical codes and scales).
+@pytest.mark.parametrize("M,K,seg_n,act_bits,bits,group,had", [
+    (1, 4096, [4096, 4096, 4096], 8, [4, 3, 3], 128, False),
+    (16, 1024, [256, 128, 128], 4, [8, 3, 3], 64, True),
+    (5, 2048, [128, 384, 128], 8, [4, 3, 3], 128, True),
+    (16, 4096, [4096, 1024, 1024], 4, [4, 3, 3], 128, False),
+])
+def test_qkv_states_decode_match_oracle(tb, M, K, seg_n, act_bits, bits, group, had):
+    say(f"  qkv states decode M={M} K={K} seg_n={seg_n} act_bits={act_bits} bits={bits} group={group} had={had}")
+    x = si.wo_activations(M, K) if had else si.normal(si.seed_for(9, 6) + M, M * K).reshape(M, K)
+    if M > 2:
+        x[M // 2] = 0.0                               # a zero row: every group zero
+    Ws = [si.gaussian_weights(9, n, K, layer=40 + s, std=0.01 * (s + 1)) for s, n in enumerate(seg_n)]
+    packed, gs = tb.bitnet_pack_weights_segments(np.concatenate(Ws), seg_n)
+    ots = [oracle.ternarize(W) for W in Ws]
+    pw = dev(packed)
+    codes, scales, q, s = _gpu_codes(tb, x, act_bits, had)
+    sc, ss = tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, act_bits, pw, gs, bits, group)
+    fc, fs = tb.hbitlinear_forward_qkv_states(dev(x), seg_n, act_bits, had, pw, gs, bits, group)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, fc) and torch.equal(ss, fs)
+    ec, es = _states_reference(q, s, [t for t, _ in ots], gs, seg_n, bits, group)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ec)
+    np.testing.assert_array_equal(ss.cpu().numpy(), es)
+    if M > 2:
+        assert np.all(sc.cpu().numpy()[M // 2] == 0) and np.all(ss.cpu().numpy()[M // 2] == 0)
+
+
 # The block's Q, K and V at full size (M = 16384, K = 4096, three 4096-row segments), launched
 # with the states fused as the benchmark does: Q at 4 bits, K and V at 3, heads of 128; one
 # sampled row in every 512-row tile of the kernel plus the whole last tile's first and last
