@@ -223,10 +223,9 @@ int hbitlinear_forward_segments(const float *x, int M, int K, int S, const int *
  * state_codes (device): M x sum(seg_n) int8, one code per byte, row-major; state_scales
  * (device): M x (sum(seg_n) / group) fp32, group j of row m at m * (sum seg_n / group) + j.
  * seg_n, w_scales, state_bits are host arrays of S entries; state_bits[s] in [2, 8]; group is
- * 64 or 128 and divides every seg_n[s].  Built for the batched case with INT4 activations
- * (M > 16; other act_bits there return BITNET_ERR_UNSUPPORTED) and for decode shapes (M <= 16,
- * INT8 or INT4 activations: the new tokens' states a low-bit KV cache appends each step).
- * Other rules, the packed weights and the workspace as hbitlinear_forward_segments. */
+ * 64 or 128 and divides every seg_n[s].  INT8 or INT4 activations, batched shapes and decode
+ * shapes (M <= 16: the new tokens' states a low-bit KV cache appends each step).  Other rules,
+ * the packed weights and the workspace as hbitlinear_forward_segments. */
 int hbitlinear_forward_qkv_states(const float *x, int M, int K, int S, const int *seg_n,
                                   int act_bits, int use_hadamard, const uint8_t *packed_w,
                                   const float *w_scales, const int *state_bits, int group,

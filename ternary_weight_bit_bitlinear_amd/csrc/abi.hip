@@ -104,9 +104,10 @@ int segment_form(int S, const int* seg_n, const float* w_scales, int* n_total, O
 }
 
 // Low-bit states of stacked linears: the segments' form plus, per segment, the states' Qp,
-// and the group (head) size.  Built for the INT4 large-M product kernel (act_bits 4, M > 16),
-// whose wave tile of 128 columns holds whole groups of 64 or 128, and for the decode streaming
-// kernel (M <= 16, INT8 or INT4), whose workgroup holds whole groups of 64 or 128.
+// and the group (head) size (64 or 128).  Every product kernel has the form: the INT4
+// large-M kernel (a wave's 128 columns hold whole groups), the INT8 one (a group of 128 spans
+// two waves' 64 columns, combined through LDS) and the decode streaming kernel (one group per
+// workgroup).
 int states_form(int S, const int* seg_n, const float* w_scales, const int* state_bits, int group,
                 int M, int act_bits, float* state_scales, int* n_total, OutForm* of)
 {
@@ -119,7 +120,6 @@ int states_form(int S, const int* seg_n, const float* w_scales, const int* state
         if (state_bits[s] < 2 || state_bits[s] > 8) return BITNET_ERR_UNSUPPORTED;
         of->seg_qp[s] = (1 << (state_bits[s] - 1)) - 1;
     }
-    if (M > 16 && act_bits != 4) return BITNET_ERR_UNSUPPORTED;
     of->states = 1;
     of->state_tiles = group / 16;
     of->state_scales = state_scales;

@@ -346,6 +346,75 @@ __device__ __forceinline__ void store_tiles_states(const v4i (&acc)[FM][FN], int
     }
 }
 
+// store_tiles_states for a group (head) of 2 FN tiles split over this wave and a partner wave
+// holding the same rows and the next FN tiles (or the previous): the maxima of every row over
+// this wave's tiles and lanes are formed first and exchanged through xch (FM * 16 floats per
+// wave, at slot 16 FM wave; the caller's LDS, free of other use, every wave of the workgroup
+// taking part); then each output is quantised with the group's maximum and stored, and the
+// wave holding the group's first columns (first) stores the scales.
+template <int FM, int FN, int SHIFT, typename ScaleFn, typename WScaleFn>
+__device__ __forceinline__ void store_tiles_states_pair(const v4i (&acc)[FM][FN], int row0, int col0, int lane,
+                                                        int M, int N, ScaleFn sxf, WScaleFn wsf,
+                                                        const OutForm& of, void* cbase, float* xch,
+                                                        int wave, int partner, bool first)
+{
+    const int g = lane >> 4;
+    const auto crs = __builtin_amdgcn_make_buffer_rsrc(cbase, 0, 0x7FFFFFFF, 0x00020000);
+    const auto srs = __builtin_amdgcn_make_buffer_rsrc((void*)of.state_scales, 0, 0x7FFFFFFF, 0x00020000);
+    const int ngroups = N / (32 * FN);
+    const int grp = (first ? col0 : col0 - 16 * FN) / (32 * FN);
+    float wsv[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+        wsv[fn] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsf(fn))));
+    const int qp = __builtin_amdgcn_readfirstlane(group_qp(of, col0 / 16));
+    auto yv = [&](int fm, int fn, int r, float sx) __attribute__((always_inline)) {
+        return ((float)(acc[fm][fn][r] >> SHIFT) * sx) * wsv[fn];
+    };
+    float amax[FM][4];
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            float a = 0.0f;
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++) a = fmaxf(a, fabsf(yv(fm, fn, r, sx[r])));
+            amax[fm][r] = max16(a);
+        }
+    }
+    __syncthreads();                  // every wave is past its last operand read of xch's LDS
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) xch[16 * FM * wave + 16 * fm + 4 * g + r] = amax[fm][r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const f4 sx = sxf(fm);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = row0 + 16 * fm + 4 * g + r;
+            const float a = fmaxf(amax[fm][r], xch[16 * FM * partner + 16 * fm + 4 * g + r]);
+            const float inv = a > 0.0f ? (float)qp / a : 0.0f;        // IEEE division
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++) {
+                const int col = col0 + 16 * fn + (lane & 15);
+                int q = (int)__builtin_rintf(yv(fm, fn, r, sx[r]) * inv);   // round half to even
+                q = q > qp ? qp : (q < -qp - 1 ? -qp - 1 : q);
+                const uint32_t off = (row < M && col < N) ? (uint32_t)(row * N + col) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q, crs, (int)off, 0, 0);
+            }
+            const float sc = a > 0.0f ? a / (float)qp : 0.0f;
+            const uint32_t soff = (first && row < M && grp < ngroups && (lane & 15) == 0)
+                                      ? 4u * (uint32_t)(row * ngroups + grp) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), srs, (int)soff, 0, 0);
+        }
+    }
+}
+
 // Nibbles (two's complement) in the low half of each byte -> int8 in each byte:
 // ((n ^ 8) + 0x78) ^ 0x80 stays within the byte, so four lanes go at once.
 __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
@@ -357,7 +426,7 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t n)
 // one weight scale per layer; a scale per row segment; gate / up pairs.
 enum Epi { kPlain = 0, kSegments = 1, kGlu = 2, kStates = 3 };
 
-template <int BITS, bool DEQ, int EPI>
+template <int BITS, bool DEQ, int EPI, int SG = 0>
 __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
 {
     __shared__ __align__(16) uint8_t As[2][BM * LROW];
@@ -525,7 +594,20 @@ __global__ __launch_bounds__(NT) void gemm_tern_kernel(LargeArgs args)
     }
     const int col0 = n0 + wn * 64;
     auto sxf = [&](int fm) __attribute__((always_inline)) { return sxr[fm]; };
-    if constexpr (EPI == kGlu)
+    if constexpr (EPI == kStates) {
+        // Low-bit states: a wave holds 64 columns, a head of 64 (SG = 4) or half of one of
+        // 128 (SG = 8) whose other half is the wave of the neighbouring column quarter and
+        // the same rows (wave ^ 2); the operand buffers, no longer read, carry the exchange.
+        static_assert(DEQ && (SG == 4 || SG == 8), "states: fp32 epilogue, heads of 64 or 128");
+        auto wsf = [&](int fn) __attribute__((always_inline)) { return group_scale(args.of, col0 / 16 + fn, w_scale); };
+        if constexpr (SG == 4)
+            store_tiles_states<8, 4, 0, 4>(acc, m0 + wm * 128, col0, lane, M, N, sxf, wsf, args.of,
+                                           (void*)args.out);
+        else
+            store_tiles_states_pair<8, 4, 0>(acc, m0 + wm * 128, col0, lane, M, N, sxf, wsf, args.of,
+                                             (void*)args.out, reinterpret_cast<float*>(&As[0][0]), wave,
+                                             wave ^ 2, (wn & 1) == 0);
+    } else if constexpr (EPI == kGlu)
         store_tiles_glu<8, 4, 0>(acc, m0 + wm * 128, col0, lane, M, N / 2, sxf, args.of.gate_scale,
                                  args.of.up_scale, obase);
     else if constexpr (EPI == kSegments)
@@ -892,7 +974,7 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
         4 * (int64_t)M * N >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     LargeArgs a{codes, scales, wptrs, w0, wscales, wscale0, out_f32, acc_i32, M, K, N, of, 0};
-    if (of.states && (bits != 4 || L != 1 || out_f32 == nullptr || of.nseg == 0 ||
+    if (of.states && (L != 1 || out_f32 == nullptr || of.nseg == 0 ||
                       (of.state_tiles != 4 && of.state_tiles != 8) || N % (16 * of.state_tiles) != 0))
         return hipErrorInvalidValue;
     if (bits == 4) {
@@ -906,7 +988,9 @@ hipError_t launch_gemm_large(const uint8_t* codes, int L, int M, int K, int N, i
         else hipLaunchKernelGGL((gemm_tern4_kernel<false, kPlain>), grid, dim3(NT4), 0, stream, a);
     } else {
         dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, L);
-        if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kGlu>), grid, dim3(NT), 0, stream, a);
+        if (of.states && of.state_tiles == 8) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kStates, 8>), grid, dim3(NT), 0, stream, a);
+        else if (of.states) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kStates, 4>), grid, dim3(NT), 0, stream, a);
+        else if (out_f32 != nullptr && of.glu) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kGlu>), grid, dim3(NT), 0, stream, a);
         else if (out_f32 != nullptr && of.nseg > 0) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kSegments>), grid, dim3(NT), 0, stream, a);
         else if (out_f32 != nullptr) hipLaunchKernelGGL((gemm_tern_kernel<8, true, kPlain>), grid, dim3(NT), 0, stream, a);
         else hipLaunchKernelGGL((gemm_tern_kernel<8, false, kPlain>), grid, dim3(NT), 0, stream, a);

@@ -354,14 +354,12 @@ def test_qkv_states_validation():
     assert f(*args(grp=32)) == tb.BITNET_ERR_UNSUPPORTED             # group 64 or 128
     assert f(*args(n=odd)) == tb.BITNET_ERR_UNSUPPORTED              # 64 rows: not whole groups
     assert f(*args(bits=bad_b)) == tb.BITNET_ERR_UNSUPPORTED         # 1-bit states
-    assert f(*args(act=8)) == tb.BITNET_ERR_UNSUPPORTED              # batched: INT4 activations only
-    assert f(*args(M=17, act=8)) == tb.BITNET_ERR_UNSUPPORTED
-    assert f(*args(M=16, act=8, ws=16)) == tb.BITNET_ERR_WORKSPACE   # decode shapes: INT8 too
-    assert f(*args(M=1, ws=16)) == tb.BITNET_ERR_WORKSPACE
-    assert f(*args(ws=16)) == tb.BITNET_ERR_WORKSPACE
+    assert f(*args(act=6)) == tb.BITNET_ERR_UNSUPPORTED              # INT8 or INT4 activations
+    # every shape class has the form (batched and decode, INT8 and INT4): these pass the
+    # checks and stop at the workspace, before any launch
+    for M, act in ((4096, 8), (17, 8), (16, 8), (1, 4)):
+        assert f(*args(M=M, act=act, ws=16)) == tb.BITNET_ERR_WORKSPACE
     g = L.hbitlinear_gemm_qkv_states
     assert g(FAKE, FAKE, 4096, 4096, 3, n3, 4, FAKE, w3, b3, 128, NUL, FAKE, NUL) == tb.BITNET_ERR_NULL
-    assert g(FAKE, FAKE, 17, 4096, 3, n3, 8, FAKE, w3, b3, 128, FAKE, FAKE, NUL) == \
-        tb.BITNET_ERR_UNSUPPORTED
     assert g(FAKE, FAKE, 16, 4096, 3, n3, 8, FAKE, w3, b3, 32, FAKE, FAKE, NUL) == \
         tb.BITNET_ERR_UNSUPPORTED

@@ -758,17 +758,21 @@ def _states_reference(q_rows, s_rows, ts, gs, seg_n, bits, group):
     return oracle.quantize_states(y, seg_n, bits, group)
 
 
-# The states form of the INT4 large-M kernel: segment boundaries inside a 128-column tile
-# (groups of 64), ragged M, Q at 4 or 8 bits with K and V at 3; every row and column against
-# the oracle run on the GPU's own activation codes (bit-identical codes and scales), and the
-# whole call against the oracle's forward on rows whose activation codes agree.
-@pytest.mark.parametrize("M,K,seg_n,bits,group,had", [
-    (300, 2048, [256, 128, 128], [4, 3, 3], 128, False),
-    (17, 512, [128, 64, 192], [8, 3, 3], 64, True),
-    (600, 4096, [512, 512, 512], [4, 3, 3], 128, True),
+# The states form of the large-M kernels (INT4: groups inside a wave's 128 columns; INT8: a
+# group of 128 over two waves' 64 columns, combined through LDS): segment boundaries inside a
+# tile (groups of 64), ragged M and N, Q at 4 or 8 bits with K and V at 3; every row and column
+# against the oracle run on the GPU's own activation codes (bit-identical codes and scales),
+# and the whole call against the oracle's forward on rows whose activation codes agree.
+@pytest.mark.parametrize("M,K,seg_n,bits,group,had,act", [
+    (300, 2048, [256, 128, 128], [4, 3, 3], 128, False, 4),
+    (17, 512, [128, 64, 192], [8, 3, 3], 64, True, 4),
+    (600, 4096, [512, 512, 512], [4, 3, 3], 128, True, 4),
+    (300, 2048, [256, 128, 128], [4, 3, 3], 128, False, 8),
+    (40, 1024, [128, 64, 192], [8, 3, 3], 64, True, 8),
+    (600, 4096, [512, 512, 640], [4, 3, 3], 128, True, 8),
 ])
-def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had):
-    say(f"  qkv states M={M} K={K} seg_n={seg_n} bits={bits} group={group} had={had}")
+def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had, act):
+    say(f"  qkv states M={M} K={K} seg_n={seg_n} bits={bits} group={group} had={had} act={act}")
     x = si.wo_activations(M, K) if had else si.normal(si.seed_for(9, 5) + M, M * K).reshape(M, K)
     x[M // 3] = 0.0                                   # a zero row: every group zero
     Ws = [si.gaussian_weights(9, n, K, layer=30 + s, std=0.01 * (s + 1)) for s, n in enumerate(seg_n)]
@@ -776,9 +780,9 @@ def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had):
     ots = [oracle.ternarize(W) for W in Ws]
     assert np.array_equal(np.asarray(gs, np.float32), np.array([g for _, g in ots], np.float32))
     pw = dev(packed)
-    codes, scales, q, s = _gpu_codes(tb, x, 4, had)
-    sc, ss = tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, 4, pw, gs, bits, group)
-    fc, fs = tb.hbitlinear_forward_qkv_states(dev(x), seg_n, 4, had, pw, gs, bits, group)
+    codes, scales, q, s = _gpu_codes(tb, x, act, had)
+    sc, ss = tb.hbitlinear_gemm_qkv_states(codes, scales, M, K, seg_n, act, pw, gs, bits, group)
+    fc, fs = tb.hbitlinear_forward_qkv_states(dev(x), seg_n, act, had, pw, gs, bits, group)
     torch.cuda.synchronize()
     assert torch.equal(sc, fc) and torch.equal(ss, fs)
     ec, es = _states_reference(q, s, [t for t, _ in ots], gs, seg_n, bits, group)
@@ -791,8 +795,8 @@ def test_qkv_states_match_oracle(tb, M, K, seg_n, bits, group, had):
         part = sc.cpu().numpy()[:, col[sgi]:col[sgi + 1]]
         assert part.min() >= -(2 ** (b - 1) - 1) and part.max() <= 2 ** (b - 1) - 1
     # end to end against the oracle's own activation stage
-    oc, os_ = oracle.forward_qkv_states(x, [oracle.pack(t) for t, _ in ots], gs, seg_n, 4, had, bits, group)
-    oq, _ = oracle.quantize(x, 4, had)
+    oc, os_ = oracle.forward_qkv_states(x, [oracle.pack(t) for t, _ in ots], gs, seg_n, act, had, bits, group)
+    oq, _ = oracle.quantize(x, act, had)
     match = np.all(oq == q, axis=1)
     assert match.mean() > 0.9
     np.testing.assert_array_equal(sc.cpu().numpy()[match], oc[match])
