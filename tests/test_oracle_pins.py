@@ -637,10 +637,12 @@ def test_states_groups_are_independent_and_scale_exactly():
     assert np.array_equal(s2[:, [0, 2, 3, 5]], s0[:, [0, 2, 3, 5]])
 
 
-def test_forward_qkv_states_hadamard_row_closed_form():
+@pytest.mark.parametrize("act", [4, 8])
+def test_forward_qkv_states_hadamard_row_closed_form(act):
     # x = a * H[j, :]: each projection's output is a sqrt(K) t_s[n, j] gamma_s (values 0 and
-    # +-gamma), so every group that holds a non-zero trit quantises to q = sign(a) Qp t_s[n, j]
-    # with scale |a| sqrt(K) gamma_s / Qp; a group of zero trits gives codes 0, scale 0
+    # +-gamma) with INT4 or INT8 activations alike (the transformed row is a spike, coded +-Qp),
+    # so every group that holds a non-zero trit quantises to q = sign(a) Qp t_s[n, j] with
+    # scale |a| sqrt(K) gamma_s / Qp; a group of zero trits gives codes 0, scale 0
     K, group = 512, 32
     seg_n, bits = [64, 32, 96], [4, 3, 3]
     H = oracle.fwht(np.eye(K, dtype=np.float32))
@@ -650,7 +652,7 @@ def test_forward_qkv_states_hadamard_row_closed_form():
         packs.append(p); gammas.append(g); ts.append(t)
     for j, a in ((3, 1.25), (K - 2, -0.5)):
         x = (np.float32(a) * H[j])[None, :]
-        codes, scales = oracle.forward_qkv_states(x, packs, gammas, seg_n, 4, True, bits, group)
+        codes, scales = oracle.forward_qkv_states(x, packs, gammas, seg_n, act, True, bits, group)
         col = 0
         for s, n in enumerate(seg_n):
             qp = 2 ** (bits[s] - 1) - 1
